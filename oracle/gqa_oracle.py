@@ -1,0 +1,130 @@
+"""Plain fp64 CPU oracle for the grouped-query attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in the
+repository's entry module and the CPU-baseline leg of the benchmark may import
+this module.  The product path (the HIP library and its Python binding) never
+imports, calls or falls back to it, and this module imports nothing from the
+product path.
+
+What it computes, and where each step comes from:
+
+* "28. Grouped-Query Attention (GQA)", sections *Problem*, *Step-by-Step
+  Approach* and *Reference solution*: the group size is read off the shapes
+  (query heads divided by KV heads, which must divide exactly), K and V are
+  expanded to the query-head count by duplicating each KV head `group` times
+  contiguously (repeat-interleave, so query head h reads KV head h // group),
+  scores are q . k / sqrt(head_dim), a (batch, seq_q, seq_k) boolean mask is
+  broadcast over heads with False meaning "set the score to -inf", a softmax
+  runs over the key axis and the weights multiply V.
+* "Multi-Query Attention", section *Implementation*: the same interface with
+  q [B, H, N, D], k/v [B, H_kv, M, D] and H % H_kv == 0.
+* "Grouped-Query Attention Explained Simply", section *Minimal
+  implementation*: self-attention with a causal mask.  Causal visibility is
+  read as "key j is visible to query i iff j <= i" for any N and M
+  (top-left aligned), combined with an explicit mask by logical AND.
+
+The page's recipe yields NaN for a query row that sees no key (softmax over an
+empty set: -inf minus -inf); the oracle keeps that NaN on purpose.
+
+Everything runs in float64 with numpy; inputs are widened exactly (bf16 and
+fp32 values are representable in fp64).  K and V are materialised in their
+expanded [B, H, M, D] form per batch row, exactly as the pages describe, with
+no blocking, fusion or reordering.  The code is deliberately slow and plain.
+
+Parity status: every function here is pinned by the CPU tests in
+tests/test_oracle.py (library cross-check, closed forms, invariants,
+brute force and planted-mistake checks); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["validate_shapes", "group_size", "expand_kv", "visibility",
+           "attention_weights", "gqa"]
+
+
+def validate_shapes(q, k, v, mask=None):
+    """Shape rules of the *Problem* section of "28. Grouped-Query Attention
+    (GQA)" and of the docstring in *Implementation* of "Multi-Query
+    Attention": q [B,H,N,D], k and v [B,H_kv,M,D], H a multiple of H_kv,
+    optional mask [B,N,M]."""
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, heads, seq, head_dim]")
+    B, H, N, D = q.shape
+    Bk, H_kv, M, Dk = k.shape
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if Bk != B or Dk != D:
+        raise ValueError("batch and head_dim of q and k/v must agree")
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("query heads must be an exact multiple of KV heads")
+    if mask is not None and tuple(mask.shape) != (B, N, M):
+        raise ValueError("mask must be [B, N, M]")
+    return B, H, H_kv, N, M, D
+
+
+def group_size(H, H_kv):
+    """Group size from the shapes alone (*Step-by-Step Approach*, step 1)."""
+    return H // H_kv
+
+
+def expand_kv(x, group):
+    """Repeat-interleave along the head axis (*Step-by-Step Approach*,
+    step 2): each KV head is duplicated `group` times contiguously, so the
+    expanded head h holds KV head h // group.  This is np.repeat, not np.tile
+    (the *Key Functions & Tricks* section warns against tiling)."""
+    return np.repeat(x, group, axis=1)
+
+
+def visibility(B, N, M, mask=None, causal=False):
+    """Boolean [B, N, M]: True where query i may attend to key j.
+
+    mask: True = attend (the reference solution fills ~mask with -inf).
+    causal: key j visible to query i iff j <= i (self-attention causal mask of
+    "Grouped-Query Attention Explained Simply", read top-left aligned).
+    Both together combine by AND."""
+    vis = np.ones((B, N, M), dtype=bool)
+    if mask is not None:
+        vis &= np.asarray(mask, dtype=bool)
+    if causal:
+        i = np.arange(N)[:, None]
+        j = np.arange(M)[None, :]
+        vis &= (j <= i)[None, :, :]
+    return vis
+
+
+def attention_weights(q, k, mask=None, causal=False):
+    """Softmax weights [B, H, N, M] in float64 (*Step-by-Step Approach*,
+    steps 3-4; *Reference solution*).  Rows with no visible key are NaN."""
+    B, H, H_kv, N, M, D = validate_shapes(q, k, k, mask)
+    g = group_size(H, H_kv)
+    vis = visibility(B, N, M, mask, causal)
+    out = np.empty((B, H, N, M), dtype=np.float64)
+    for b in range(B):
+        qb = np.asarray(q[b], dtype=np.float64)                  # [H, N, D]
+        kb = expand_kv(np.asarray(k[b:b + 1], dtype=np.float64), g)[0]  # [H, M, D]
+        scores = np.matmul(qb, kb.transpose(0, 2, 1)) / math.sqrt(D)   # [H, N, M]
+        scores = np.where(vis[b][None, :, :], scores, -np.inf)
+        with np.errstate(invalid="ignore"):
+            row_max = scores.max(axis=-1, keepdims=True)
+            e = np.exp(scores - row_max)
+            out[b] = e / e.sum(axis=-1, keepdims=True)
+    return out
+
+
+def gqa(q, k, v, mask=None, causal=False):
+    """O = softmax(Q K^T / sqrt(D) [masked]) V with repeat-interleave head
+    grouping; returns float64 [B, H, N, D].  Runs per batch row to bound
+    memory; the expanded K and V of that row are materialised."""
+    B, H, H_kv, N, M, D = validate_shapes(q, k, v, mask)
+    g = group_size(H, H_kv)
+    out = np.empty((B, H, N, D), dtype=np.float64)
+    for b in range(B):
+        w = attention_weights(q[b:b + 1], k[b:b + 1],
+                              None if mask is None else mask[b:b + 1], causal)[0]
+        vb = expand_kv(np.asarray(v[b:b + 1], dtype=np.float64), g)[0]  # [H, M, D]
+        out[b] = np.matmul(w, vb)
+    return out

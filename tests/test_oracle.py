@@ -1,0 +1,384 @@
+"""Pins for the fp64 oracle: it is checked against things other than itself.
+
+* a library routine that computes the same thing (torch's CPU
+  scaled_dot_product_attention with enable_gqa, float64);
+* closed forms (single key, two keys, all-zero keys, constant-per-head V);
+* invariants (weights sum to one, masked keys contribute nothing, padding
+  equals truncation, causal equals an explicit lower-triangular mask, key
+  permutation);
+* pure-Python brute force on tiny inputs;
+* the worked example of "28. Grouped-Query Attention (GQA)" (shape only);
+* planted mistakes: mutated copies of the oracle must fail at least one pin.
+"""
+
+import math
+import os
+import re
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import gqa_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_qkv(seed, B, H, H_kv, N, M, D, scale=1.0):
+    r = rng(seed)
+    q = r.standard_normal((B, H, N, D)) * scale
+    k = r.standard_normal((B, H_kv, M, D))
+    v = r.standard_normal((B, H_kv, M, D))
+    return q, k, v
+
+
+def brute_force(q, k, v, mask=None, causal=False):
+    """Pure-Python loops (math.exp, explicit sums) over tiny inputs."""
+    B, H, N, D = q.shape
+    H_kv, M = k.shape[1], k.shape[2]
+    g = H // H_kv
+    out = np.zeros((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            j = h // g
+            for i in range(N):
+                s = []
+                for m in range(M):
+                    ok = True
+                    if mask is not None and not mask[b][i][m]:
+                        ok = False
+                    if causal and m > i:
+                        ok = False
+                    if ok:
+                        dot = 0.0
+                        for d in range(D):
+                            dot += float(q[b, h, i, d]) * float(k[b, j, m, d])
+                        s.append((m, dot / math.sqrt(D)))
+                if not s:
+                    out[b, h, i, :] = float("nan")
+                    continue
+                mx = max(x for _, x in s)
+                w = [(m, math.exp(x - mx)) for m, x in s]
+                tot = sum(x for _, x in w)
+                for d in range(D):
+                    out[b, h, i, d] = sum(x * float(v[b, j, m, d]) for m, x in w) / tot
+    return out
+
+
+# ---------------------------------------------------------------- pin suite
+# Each pin takes an oracle module and raises AssertionError (or any error)
+# when the module disagrees with what the pages and the mathematics fix.
+
+def pin_worked_example_shape(orc):
+    shapes = {}
+    with open(os.path.join(GOLDEN, "worked_example.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, *dims = line.split()
+                shapes[name] = tuple(int(x) for x in dims)
+    r = rng(0)
+    q = r.standard_normal(shapes["q"])
+    k = r.standard_normal(shapes["k"])
+    assert orc.gqa(q, k, k).shape == shapes["out"]
+
+
+def _sdpa_ref(q, k, v, mask=None, causal=False):
+    """torch CPU SDPA in float64, grouping via enable_gqa."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    N, M = q.shape[2], k.shape[2]
+    attn = None
+    if mask is not None:
+        attn = torch.from_numpy(mask)[:, None, :, :]
+    if causal:
+        tri = torch.ones(N, M, dtype=torch.bool).tril()
+        attn = tri[None, None] if attn is None else (attn & tri[None, None])
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=attn,
+                                       enable_gqa=(q.shape[1] != k.shape[1]))
+    return o.numpy()
+
+
+LIB_CASES = [
+    # seed, B, H, H_kv, N, M, D, mask kind, causal
+    (1, 2, 4, 4, 7, 9, 8, None, False),     # MHA
+    (2, 2, 8, 2, 5, 13, 16, None, False),   # g = 4
+    (3, 1, 6, 3, 6, 6, 4, None, True),      # g = 2, causal N == M
+    (4, 2, 4, 1, 3, 11, 8, "random", False),  # MQA with mask
+    (5, 2, 8, 4, 9, 5, 12, "padding", False),
+    (6, 1, 4, 2, 8, 12, 8, "random", True),  # mask AND causal, N != M
+]
+
+
+def _mask(kind, seed, B, N, M):
+    r = rng(seed + 1000)
+    if kind is None:
+        return None
+    if kind == "random":
+        m = r.random((B, N, M)) < 0.6
+        m[:, :, 0] = True          # every row sees key 0 (SDPA differs on empty rows)
+        return m
+    lens = r.integers(1, M + 1, size=B)
+    return np.broadcast_to(np.arange(M)[None, None, :] < lens[:, None, None],
+                           (B, N, M)).copy()
+
+
+def pin_library_crosscheck(orc):
+    for seed, B, H, H_kv, N, M, D, mk, causal in LIB_CASES:
+        q, k, v = rand_qkv(seed, B, H, H_kv, N, M, D)
+        mask = _mask(mk, seed, B, N, M)
+        ref = _sdpa_ref(q, k, v, mask, causal)
+        got = orc.gqa(q, k, v, mask, causal)
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_brute_force(orc):
+    cases = [(11, 1, 4, 2, 3, 5, 3, None, False),
+             (12, 2, 2, 1, 4, 4, 2, "random", True),
+             (13, 1, 6, 2, 2, 7, 4, "padding", False),
+             (14, 1, 3, 3, 3, 3, 5, None, True)]
+    for seed, B, H, H_kv, N, M, D, mk, causal in cases:
+        q, k, v = rand_qkv(seed, B, H, H_kv, N, M, D)
+        mask = _mask(mk, seed, B, N, M)
+        np.testing.assert_allclose(orc.gqa(q, k, v, mask, causal),
+                                   brute_force(q, k, v, mask, causal),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def pin_mha_equals_per_head(orc):
+    """H_kv == H is ordinary multi-head attention ("Step-by-Step Approach",
+    sanity check): compared with torch SDPA without grouping and with the
+    brute-force loops."""
+    q, k, v = rand_qkv(21, 2, 3, 3, 4, 6, 5)
+    got = orc.gqa(q, k, v)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v))).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got, brute_force(q, k, v), rtol=1e-12, atol=1e-13)
+
+
+def pin_mqa_brute_force(orc):
+    """H_kv == 1: every query head reads the single KV head."""
+    q, k, v = rand_qkv(22, 1, 5, 1, 3, 6, 4)
+    got = orc.gqa(q, k, v)
+    for h in range(5):
+        one = brute_force(q[:, h:h + 1], k, v)
+        np.testing.assert_allclose(got[:, h:h + 1], one, rtol=1e-12, atol=1e-13)
+
+
+def pin_single_key(orc):
+    """M == 1: the softmax weight is exactly 1, so out[b,h] = v[b, h//g, 0]."""
+    q, k, v = rand_qkv(23, 2, 8, 2, 3, 1, 6)
+    got = orc.gqa(q, k, v)
+    for h in range(8):
+        assert np.array_equal(got[:, h], np.broadcast_to(v[:, h // 4, 0:1, :], (2, 3, 6)))
+
+
+def pin_two_keys_closed_form(orc):
+    """M == 2: weight of key 1 is the logistic of (s1 - s0) with
+    s = q.k / sqrt(D)."""
+    q, k, v = rand_qkv(24, 1, 4, 2, 3, 2, 9)
+    got = orc.gqa(q, k, v)
+    for h in range(4):
+        j = h // 2
+        for i in range(3):
+            s0 = float(np.dot(q[0, h, i], k[0, j, 0])) / 3.0
+            s1 = float(np.dot(q[0, h, i], k[0, j, 1])) / 3.0
+            w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+            ref = (1.0 - w1) * v[0, j, 0] + w1 * v[0, j, 1]
+            np.testing.assert_allclose(got[0, h, i], ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_scale_exact(orc):
+    """Scores carry exactly 1/sqrt(D): with D = 4, q = (2,0,0,0), k0 = e0 and
+    k1 = 0 the scores are 1 and 0, so the weights are e/(e+1) and 1/(e+1)."""
+    q = np.zeros((1, 1, 1, 4)); q[0, 0, 0, 0] = 2.0
+    k = np.zeros((1, 1, 2, 4)); k[0, 0, 0, 0] = 1.0
+    v = np.zeros((1, 1, 2, 4)); v[0, 0, 0, :] = 1.0
+    got = orc.gqa(q, k, v)
+    e = math.e
+    np.testing.assert_allclose(got[0, 0, 0], np.full(4, e / (e + 1)), rtol=1e-14)
+
+
+def pin_zero_keys_give_mean(orc):
+    """K == 0 makes all visible scores equal, so the output is the mean of
+    the visible V rows of the head's KV head (mask and causal included)."""
+    B, H, H_kv, N, M, D = 2, 6, 2, 5, 7, 3
+    q, _, v = rand_qkv(25, B, H, H_kv, N, M, D)
+    k = np.zeros((B, H_kv, M, D))
+    mask = _mask("random", 25, B, N, M)
+    got = orc.gqa(q, k, v, mask, causal=True)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                vis = [m for m in range(M) if mask[b, i, m] and m <= i]
+                ref = v[b, h // 3, vis].mean(axis=0)
+                np.testing.assert_allclose(got[b, h, i], ref, rtol=1e-12, atol=1e-14)
+
+
+def pin_head_mapping_exact(orc):
+    """K == 0 and V[b, j] == j: query head h must return exactly h // g
+    (repeat-interleave); the tiled mapping h % H_kv would differ.  M is a
+    power of two so that the equal weights 1/M are exact in binary."""
+    for H, H_kv in [(8, 2), (12, 4), (6, 3), (4, 4), (5, 1)]:
+        g = H // H_kv
+        q = rng(26).standard_normal((2, H, 3, 4))
+        k = np.zeros((2, H_kv, 8, 4))
+        v = np.broadcast_to(np.arange(H_kv, dtype=np.float64)[None, :, None, None],
+                            (2, H_kv, 8, 4)).copy()
+        got = orc.gqa(q, k, v)
+        for h in range(H):
+            assert np.all(got[:, h] == h // g), (H, H_kv, h)
+
+
+def pin_weights_sum_to_one(orc):
+    q, k, _ = rand_qkv(27, 2, 8, 4, 6, 10, 8, scale=3.0)
+    mask = _mask("random", 27, 2, 6, 10)
+    w = orc.attention_weights(q, k, mask, causal=True)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(w >= 0)
+    # masked or future keys get exactly zero weight
+    vis = mask[:, None] & (np.arange(10)[None, :] <= np.arange(6)[:, None])[None, None]
+    assert np.all(w[~np.broadcast_to(vis, w.shape)] == 0.0)
+
+
+def pin_masked_keys_contribute_nothing(orc):
+    B, H, H_kv, N, M, D = 2, 4, 2, 5, 9, 6
+    q, k, v = rand_qkv(28, B, H, H_kv, N, M, D)
+    lens = np.array([4, 7])
+    mask = np.arange(M)[None, None, :] < lens[:, None, None]
+    mask = np.broadcast_to(mask, (B, N, M)).copy()
+    a = orc.gqa(q, k, v, mask)
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        k2[b, :, lens[b]:] = 1e3 * rng(29).standard_normal(k2[b, :, lens[b]:].shape)
+        v2[b, :, lens[b]:] = -7.0
+    assert np.array_equal(a, orc.gqa(q, k2, v2, mask))
+    # padding mask equals attention over the truncated key set
+    for b in range(B):
+        t = orc.gqa(q[b:b + 1], k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]])
+        np.testing.assert_allclose(a[b:b + 1], t, rtol=1e-13, atol=1e-14)
+
+
+def pin_causal_properties(orc):
+    B, H, H_kv, N, D = 2, 4, 2, 6, 5
+    q, k, v = rand_qkv(30, B, H, H_kv, N, N, D)
+    c = orc.gqa(q, k, v, causal=True)
+    tri = np.broadcast_to(np.tril(np.ones((N, N), dtype=bool)), (B, N, N)).copy()
+    np.testing.assert_allclose(c, orc.gqa(q, k, v, tri), rtol=1e-14, atol=1e-15)
+    full = orc.gqa(q, k, v)
+    np.testing.assert_allclose(c[:, :, -1], full[:, :, -1], rtol=1e-13, atol=1e-14)
+    for h in range(H):
+        assert np.array_equal(c[:, h, 0], v[:, h // 2, 0])
+    # N != M: causal is top-left (key j visible to query i iff j <= i)
+    q2, k2, v2 = rand_qkv(31, 1, 2, 1, 3, 7, 4)
+    c2 = orc.gqa(q2, k2, v2, causal=True)
+    for i in range(3):
+        sub = orc.gqa(q2[:, :, i:i + 1], k2[:, :, :i + 1], v2[:, :, :i + 1])
+        np.testing.assert_allclose(c2[:, :, i:i + 1], sub, rtol=1e-13, atol=1e-14)
+
+
+def pin_key_permutation(orc):
+    B, H, H_kv, N, M, D = 1, 4, 2, 3, 8, 4
+    q, k, v = rand_qkv(32, B, H, H_kv, N, M, D)
+    mask = _mask("random", 32, B, N, M)
+    perm = rng(33).permutation(M)
+    a = orc.gqa(q, k, v, mask)
+    b = orc.gqa(q, k[:, :, perm], v[:, :, perm], mask[:, :, perm])
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+def pin_empty_row_is_nan(orc):
+    """A row with no visible key follows the reference solution's recipe
+    (softmax of all -inf), i.e. NaN; rows that see keys stay finite."""
+    q, k, v = rand_qkv(34, 1, 4, 2, 3, 4, 4)
+    mask = np.ones((1, 3, 4), dtype=bool)
+    mask[0, 1, :] = False
+    o = orc.gqa(q, k, v, mask)
+    assert np.all(np.isnan(o[0, :, 1]))
+    assert np.all(np.isfinite(o[0, :, 0])) and np.all(np.isfinite(o[0, :, 2]))
+
+
+def pin_rejects_bad_group(orc):
+    q, k, v = rand_qkv(35, 1, 6, 4, 2, 3, 4)
+    with pytest.raises(ValueError):
+        orc.gqa(q, k, v)
+
+
+PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
+        pin_mha_equals_per_head, pin_mqa_brute_force, pin_single_key,
+        pin_two_keys_closed_form, pin_scale_exact, pin_zero_keys_give_mean,
+        pin_head_mapping_exact, pin_weights_sum_to_one,
+        pin_masked_keys_contribute_nothing, pin_causal_properties,
+        pin_key_permutation, pin_empty_row_is_nan, pin_rejects_bad_group]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(gqa_oracle)
+
+
+def test_tiling_differs():
+    """The tiled head mapping used by one page (K.repeat over heads) gives a
+    different answer whenever 1 < H_kv < H, so the two readings are
+    distinguishable on random inputs."""
+    for H, H_kv in [(4, 2), (8, 2), (6, 3), (8, 4)]:
+        q, k, v = rand_qkv(40 + H, 1, H, H_kv, 4, 6, 8)
+        g = H // H_kv
+        tiled = oracle.gqa(q, np.tile(k, (1, g, 1, 1)), np.tile(v, (1, g, 1, 1)))
+        inter = oracle.gqa(q, k, v)
+        assert np.max(np.abs(tiled - inter)) > 1e-3
+    # g == 1 or H_kv == 1: the two mappings coincide
+    q, k, v = rand_qkv(50, 1, 4, 1, 3, 5, 4)
+    np.testing.assert_allclose(oracle.gqa(q, np.tile(k, (1, 4, 1, 1)),
+                                          np.tile(v, (1, 4, 1, 1))),
+                               oracle.gqa(q, k, v), rtol=1e-14)
+
+
+# ------------------------------------------------------- planted mistakes
+MUTANTS = {
+    "tile_instead_of_interleave": (r"np\.repeat\(x, group, axis=1\)",
+                                   "np.tile(x, (1, group, 1, 1))"),
+    "no_scale": (r" / math\.sqrt\(D\)", ""),
+    "scale_by_D": (r"math\.sqrt\(D\)", "D"),
+    "causal_strict": (r"\(j <= i\)", "(j < i)"),
+    "causal_transposed": (r"\(j <= i\)", "(j >= i)"),
+    "mask_polarity": (r"vis &= np\.asarray\(mask, dtype=bool\)",
+                      "vis &= ~np.asarray(mask, dtype=bool)"),
+    "softmax_wrong_axis": (r"e / e\.sum\(axis=-1, keepdims=True\)",
+                           "e / e.sum(axis=-2, keepdims=True)"),
+    "v_from_k": (r"vb = expand_kv\(np\.asarray\(v\[", "vb = expand_kv(np.asarray(k["),
+    "group_from_kv": (r"return H // H_kv", "return max(1, H_kv // H)"),
+    "max_not_subtracted_wrong_sign": (r"np\.exp\(scores - row_max\)",
+                                      "np.exp(row_max - scores)"),
+    "mask_ignored": (r"vis &= np\.asarray\(mask, dtype=bool\)", "pass"),
+    "transposed_v": (r"out\[b\] = np\.matmul\(w, vb\)",
+                     "out[b] = np.matmul(w, vb.transpose(0, 2, 1)[:, :w.shape[-1], :]) if vb.shape[1] == vb.shape[2] else np.matmul(w, vb)[..., ::-1]"),
+}
+
+
+def _mutant(name):
+    pat, rep = MUTANTS[name]
+    src = open(gqa_oracle.__file__).read()
+    new, n = re.subn(pat, rep, src)
+    assert n >= 1, f"mutation {name} did not apply"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(new, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception:          # noqa: BLE001 - any failure counts
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"

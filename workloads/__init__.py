@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the grouped-query attention forward pass.
+
+This module holds the five workload definitions and the random-input
+generators that feed both the HIP path and the fp64 oracle.  It contains none
+of the attention arithmetic: it only draws numbers and builds the padding mask
+that defines a workload.
+
+Recipe (same bits for both sides):
+  * a CPU ``torch.Generator`` seeded with the workload's seed;
+  * draw q, then k, then v as float32 N(0, 1) in that order;
+  * cast to bfloat16 for bf16 workloads (round-to-nearest-even);
+  * padded workloads then draw one length per batch row, uniform on
+    {1, ..., M}, and key j is valid for batch row b iff j < len_b.
+
+Shapes follow the pages: Mistral-7B heads (32 query / 8 KV) and Llama-2-70B
+heads (64 / 8) from "Grouped-Query Attention Explained Simply", *Numbers to
+anchor on*; 4K and 32k contexts and batch 16 from the KV-cache figures of the
+GQA deep-dive page and of "Multi-Query Attention"; the (4, 512, d_model=768,
+32 heads, 4 KV heads) usage example of the deep-dive page's *Implementation*
+section gives head_dim 24 for the padded workload; the tiny workload is the
+worked example of "28. Grouped-Query Attention (GQA)", *Problem*.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "by_name", "make_inputs", "random_case"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    H_kv: int
+    N: int
+    M: int
+    D: int
+    dtype: str          # "fp32" or "bf16"
+    causal: bool = False
+    padded: bool = False  # padding mask j < len_b, len_b ~ U{1..M}
+
+    @property
+    def kind(self) -> str:
+        return "decode" if self.N == 1 and not self.causal else "prefill"
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+
+WORKLOADS = [
+    Workload("tiny_fp32", 1, 1, 4, 2, 5, 5, 4, "fp32"),
+    Workload("decode_mistral7b_m4096", 2, 16, 32, 8, 1, 4096, 128, "bf16"),
+    Workload("decode_llama70b_m32768", 3, 16, 64, 8, 1, 32768, 128, "bf16"),
+    Workload("prefill_causal_n4096", 4, 4, 32, 8, 4096, 4096, 128, "bf16",
+             causal=True),
+    Workload("prefill_padded_d24", 5, 4, 32, 4, 512, 512, 24, "fp32",
+             padded=True),
+]
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def _draw(gen, B, H, H_kv, N, M, D, dtype):
+    q = torch.randn((B, H, N, D), generator=gen, dtype=torch.float32)
+    k = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
+    v = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
+    if dtype == torch.bfloat16:
+        q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    return q, k, v
+
+
+def padding_mask(lengths, N, M):
+    """mask[b, i, j] = j < lengths[b] (True = key valid), shape [B, N, M]."""
+    j = torch.arange(M)
+    row = j[None, :] < lengths[:, None]                     # [B, M]
+    return row[:, None, :].expand(len(lengths), N, M).contiguous()
+
+
+def make_inputs(w: Workload):
+    """Return (q, k, v, mask, causal) as CPU tensors for workload ``w``.
+
+    mask is a bool tensor [B, N, M] or None."""
+    gen = torch.Generator().manual_seed(w.seed)
+    q, k, v = _draw(gen, w.B, w.H, w.H_kv, w.N, w.M, w.D, w.torch_dtype)
+    mask = None
+    if w.padded:
+        lengths = torch.randint(1, w.M + 1, (w.B,), generator=gen)
+        mask = padding_mask(lengths, w.N, w.M)
+    return q, k, v, mask, w.causal
+
+
+def random_case(seed, B, H, H_kv, N, M, D, dtype=torch.float32,
+                mask_kind=None, q_scale=1.0):
+    """Small randomized case for parity sweeps.
+
+    mask_kind: None, "padding" (j < len_b), "random" (i.i.d. Bernoulli(0.7)
+    per [b, i, j]) or "blocks" (whole 64-key column blocks switched off at
+    random, to exercise skipped tiles).  q_scale multiplies q before the
+    cast, to make peaky score rows."""
+    gen = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, N, D), generator=gen, dtype=torch.float32) * q_scale
+    k = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
+    v = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
+    if dtype == torch.bfloat16:
+        q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
+    mask = None
+    if mask_kind == "padding":
+        lengths = torch.randint(1, M + 1, (B,), generator=gen)
+        mask = padding_mask(lengths, N, M)
+    elif mask_kind == "random":
+        mask = torch.rand((B, N, M), generator=gen) < 0.7
+    elif mask_kind == "blocks":
+        nblk = (M + 63) // 64
+        on = torch.rand((B, nblk), generator=gen) < 0.5
+        on[:, 0] = True
+        cols = on.repeat_interleave(64, dim=1)[:, :M]        # [B, M]
+        mask = cols[:, None, :].expand(B, N, M).contiguous()
+    elif mask_kind is not None:
+        raise ValueError(mask_kind)
+    return q, k, v, mask
