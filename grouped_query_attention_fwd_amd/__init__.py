@@ -1,0 +1,189 @@
+"""Grouped-query attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of libgqa.so (include/gqa.h).  It only
+marshals arguments: torch tensors become device pointers and the current HIP
+stream is passed through; every step of the computation runs in the HIP
+kernels.  There is no CPU fallback: if the library is missing or the tensors
+are not on a GPU the call raises.
+
+    decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None)
+        q [B,H,1,D], k/v [B,H_kv,M,D], mask [B,1,M] bool/uint8 or None
+    prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None)
+        q [B,H,N,D], k/v [B,H_kv,M,D], mask [B,N,M] bool/uint8 or None
+    decode_workspace_size(B, H, H_kv, M, D) -> bytes
+    status_string(code) -> str
+
+Query head h reads KV head h // (H // H_kv) (repeat-interleave grouping),
+scores are scaled by 1/sqrt(D), a mask entry that is False/0 hides the key
+from every head, and causal means key j is visible to query i iff j <= i.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["decode", "prefill", "decode_workspace_size", "status_string",
+           "library_path", "GQAError", "load_library"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgqa.so")
+_lib = None
+
+GQA_F32, GQA_BF16 = 0, 1
+_STATUS_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9}
+
+
+class GQAError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"gqa status {code}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgqa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not built: {_LIB_PATH} is missing "
+            "(build it with `python -m grouped_query_attention_fwd_amd._build`)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.gqa_decode.restype = i
+    lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, vp]
+    lib.gqa_prefill.restype = i
+    lib.gqa_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.gqa_decode_workspace_size.restype = sz
+    lib.gqa_status_string.argtypes = [i]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().gqa_status_string(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        msg = status_string(code)
+        if code in _STATUS_VALUE_ERRORS:
+            raise ValueError(f"gqa status {code}: {msg}")
+        raise GQAError(code, msg)
+
+
+def decode_workspace_size(B, H, H_kv, M, D) -> int:
+    return int(load_library().gqa_decode_workspace_size(B, H, H_kv, M, D))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t == torch.float32:
+        return GQA_F32
+    if t == torch.bfloat16:
+        return GQA_BF16
+    raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _check_tensors(q, k, v, mask):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU (no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same dtype")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be [B,H_kv,M,D] with q's B and D")
+    if mask is not None:
+        if not mask.is_cuda or mask.device != q.device:
+            raise ValueError("mask must be on the same GPU as q")
+        if not mask.is_contiguous():
+            raise ValueError("mask must be contiguous")
+        if mask.dtype not in (torch.bool, torch.uint8):
+            raise ValueError("mask must be bool or uint8")
+
+
+def _mask_ptr(mask):
+    if mask is None:
+        return None
+    # bool and uint8 share the one-byte layout; nonzero = visible
+    return mask.data_ptr()
+
+
+def _out(q, out, out_dtype, shape):
+    torch = _torch()
+    od = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(shape, dtype=od, device=q.device)
+    else:
+        if tuple(out.shape) != tuple(shape) or out.dtype != od or not out.is_contiguous() \
+                or out.device != q.device:
+            raise ValueError("out has the wrong shape, dtype, device or layout")
+    return out
+
+
+def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
+    """One decode step; see the module docstring.  workspace: optional
+    uint8 device tensor of at least decode_workspace_size(...) bytes (no
+    initialisation needed); allocated per call when omitted."""
+    torch = _torch()
+    _check_tensors(q, k, v, mask)
+    B, H, N, D = q.shape
+    _, H_kv, M, _ = k.shape
+    if N != 1:
+        raise ValueError("decode takes one query position (q [B,H,1,D])")
+    if mask is not None and tuple(mask.shape) != (B, 1, M):
+        raise ValueError("decode mask must be [B,1,M]")
+    out = _out(q, out, out_dtype, (B, H, 1, D))
+    lib = load_library()
+    need = int(lib.gqa_decode_workspace_size(B, H, H_kv, M, D))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        code = lib.gqa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask),
+                              out.data_ptr(), B, H, H_kv, M, D, _dtype_code(q.dtype),
+                              _dtype_code(out.dtype), ws_ptr, ws_bytes, stream)
+    _check(code)
+    return out
+
+
+def prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
+    """Prefill forward; see the module docstring."""
+    torch = _torch()
+    _check_tensors(q, k, v, mask)
+    B, H, N, D = q.shape
+    _, H_kv, M, _ = k.shape
+    if mask is not None and tuple(mask.shape) != (B, N, M):
+        raise ValueError("prefill mask must be [B,N,M]")
+    out = _out(q, out, out_dtype, (B, H, N, D))
+    lib = load_library()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        code = lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask),
+                               1 if causal else 0, out.data_ptr(), B, H, H_kv, N, M, D,
+                               _dtype_code(q.dtype), _dtype_code(out.dtype), stream)
+    _check(code)
+    return out

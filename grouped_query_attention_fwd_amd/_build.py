@@ -1,0 +1,64 @@
+"""Build step for libgqa.so (hipcc, gfx950).  Run as a module or through the
+repository's build() entry point; it always recompiles."""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgqa.so")
+SOURCES = ["gqa_api.hip", "decode.hip", "prefill.hip"]
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Wno-unused-function",
+    # keep the compiler from forming packed fp32 VALU ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; drop that noise
+    out = "\n".join(line for line in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+        outs = list(ex.map(_run, cmds))
+    vers = os.path.join(BUILD, "exports.map")
+    with open(vers, "w") as f:
+        f.write("{ global: gqa_*; local: *; };\n")
+    tmp = LIB + ".tmp"
+    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+                      f"-Wl,--version-script={vers}"]))
+    os.replace(tmp, LIB)
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,423 @@
+// Decode (one query position) grouped-query attention forward for gfx950.
+//
+// Operation: for each batch row b and query head h,
+//   o[b,h,:] = softmax_j(q[b,h,:] . k[b,h/g,j,:] / sqrt(D)) v[b,h/g,j,:]
+// ("28. Grouped-Query Attention (GQA)", *Reference solution*, with the
+// grouping done as a zero head stride as "Multi-Query Attention",
+// *Implementation*, describes for real kernels).
+//
+// Why it is shaped this way: decode re-reads the whole KV cache once per
+// step and does ~g flop per byte ("Multi-Query Attention", *Theory*), so the
+// kernel is HBM-bound.  Each K and V row is read from HBM exactly once and
+// used for all the query heads of its group (up to 16 per workgroup).
+//
+// Work split: one workgroup of four waves per (batch row, KV head, chunk of
+// up to 16 query heads, key range "split").  Inside a workgroup the waves
+// take interleaved chunks of KC keys.  Per chunk a wave
+//   1. loads K rows straight into MFMA operand registers (16 bytes per lane)
+//      and V rows with coalesced 16-byte loads, all issued up front with
+//      clamped (always valid) addresses so nothing waits on a branch;
+//   2. forms S^T = K Q^T on the matrix cores (keys x heads);
+//   3. copies the V chunk into its private, XOR-swizzled LDS area;
+//   4. runs the online softmax with scores scaled by log2(e)/sqrt(D) and the
+//      hardware exp2; lane l%16 owns head l%16, so the running max and the
+//      rescale factor stay in the lane and the row max needs two cross-lane
+//      steps;
+//   5. forms O^T += V^T P^T on the matrix cores, reading V^T from LDS with
+//      the transposing ds_read_b64_tr_b16 (bf16) or plain reads (fp32).
+// The four waves merge (m, l, acc) through LDS.  With one split the result is
+// written directly.  Otherwise every workgroup stores its (m, l, acc) partial
+// to the fp32 workspace and a second small kernel merges the splits of each
+// head in split order.  The merge order is fixed, so results are
+// bit-reproducible, and no cross-workgroup synchronisation is needed.
+#include "gqa_device.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
+// Workgroups to aim for when choosing the split count.
+#ifndef GQA_DECODE_TARGET_WGS
+#define GQA_DECODE_TARGET_WGS 512
+#endif
+
+template <bool BF16, int DP>
+struct DecCfg {
+  static constexpr int ELT = BF16 ? 2 : 4;
+  // keys per wave chunk (bounded by LDS and by the registers of the loads)
+  static constexpr int KC = BF16 ? (DP <= 128 ? 64 : 32) : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));
+  static constexpr int NKB = KC / 16;                 // 16-key MFMA blocks per chunk
+  static constexpr int NDB = DP / 16;                 // 16-wide d blocks of O
+  static constexpr int QCH = BF16 ? DP / 32 : DP / 16;  // 16-byte Q/K chunks per lane per key
+  static constexpr int CPR = DP * ELT / 16;           // 16-byte chunks per row
+  static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16;  // LDS row stride (fp32 rows padded)
+  static constexpr int VBYTES = KC * ROWB;            // LDS bytes of one wave's V chunk
+  static constexpr int VLOADS = KC * CPR / 64;        // 16-byte V loads per lane per chunk
+  static constexpr int SPR = DP / 16;                 // 32-byte segments per bf16 row
+  static constexpr int SWZ = (SPR < 8 ? SPR : 8) - 1;
+  static constexpr int COMBINE_BYTES = kWaves * 16 * DP * 4 + 2 * kWaves * 16 * 4;
+  static constexpr int LDS_BYTES =
+      (kWaves * VBYTES > COMBINE_BYTES) ? kWaves * VBYTES : COMBINE_BYTES;
+};
+
+// Byte offset of 16-byte chunk `chunk` of LDS row `row` of a V chunk.
+template <bool BF16, int DP>
+__device__ __forceinline__ uint32_t v_off(int row, int chunk) {
+  using C = DecCfg<BF16, DP>;
+  if constexpr (BF16) {
+    return row * C::ROWB + ((chunk ^ (2 * (row & C::SWZ))) << 4);
+  } else {
+    return row * C::ROWB + (chunk << 4);
+  }
+}
+
+template <bool OUTF32>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
+  if constexpr (OUTF32) {
+    reinterpret_cast<float*>(out)[idx] = x;
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(x);
+  }
+}
+
+// EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is given.
+template <bool BF16, int DP, bool EXACT, bool MASKED, bool OUTF32>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
+  using C = DecCfg<BF16, DP>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c16 = lane & 15;
+  const int qg = lane >> 4;
+
+  const int unit = blockIdx.x;
+  const int per_b = a.H_kv * a.head_chunks;
+  const int b = unit / per_b;
+  const int rem = unit - b * per_b;
+  const int j = rem / a.head_chunks;
+  const int hc = rem - j * a.head_chunks;
+  const int h0 = j * a.g + hc * 16;
+  const int gh = min(16, a.g - hc * 16);
+  const int D = EXACT ? DP : a.D;
+  const int M = a.M;
+
+  const int s = blockIdx.y;
+  const int k_begin = s * a.keys_per_split;
+  const int k_end = min(M, k_begin + a.keys_per_split);
+
+  const size_t kv_base = ((size_t)b * a.H_kv + j) * (size_t)M * D;  // elements
+  const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
+  const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
+  const uint8_t* mrow = MASKED ? a.mask + (size_t)b * M : nullptr;
+
+  // 1/sqrt(D) folded with log2(e): p = 2^(s*sl - m*sl).
+  const float sl = kLog2e / sqrtf((float)D);
+
+  // Q operand: head h0 + c16, 16-byte chunks (zero for padding heads / d).
+  u32x4 qop[C::QCH];
+  {
+    const bool hv = c16 < gh;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     ((size_t)b * a.H + h0 + (hv ? c16 : 0)) * (size_t)D * C::ELT;
+#pragma unroll
+    for (int u = 0; u < C::QCH; ++u) {
+      const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+      const bool dv = EXACT || d0 < D;
+      qop[u] = sel16(hv && dv, ld16(qp + (size_t)(dv ? d0 : 0) * C::ELT));
+    }
+  }
+
+  float m_run = kNegInf;
+  float l_run = 0.f;  // lane-partial row sum (this lane's keys only)
+  f32x4 acc[C::NDB];
+#pragma unroll
+  for (int i = 0; i < C::NDB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  lds_char* vl = smem + w * C::VBYTES;
+  const int klast = k_end - 1;
+
+  for (int base = k_begin + w * C::KC; base < k_end; base += kWaves * C::KC) {
+    // ---- issue all loads of the chunk: K first, then V -------------------
+    u32x4 kop[C::NKB][C::QCH];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int key = min(base + 16 * kb + c16, klast);
+      const char* krow = kp + (size_t)key * D * C::ELT;
+#pragma unroll
+      for (int u = 0; u < C::QCH; ++u) {
+        const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+        if constexpr (EXACT) {
+          kop[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
+        } else {
+          const bool dv = d0 < D;
+          kop[kb][u] = sel16(dv, ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT));
+        }
+      }
+    }
+    u32x4 vreg[C::VLOADS];
+#pragma unroll
+    for (int it = 0; it < C::VLOADS; ++it) {
+      const int piece = it * 64 + lane;
+      const int row = piece / C::CPR;
+      const int chunk = piece - row * C::CPR;
+      const int key = base + row;
+      const int d0 = chunk * (16 / C::ELT);
+      const bool ok = key < k_end && (EXACT || d0 < D);
+      const u32x4 x = ld16(vp + ((size_t)min(key, klast) * D + (ok ? d0 : 0)) * C::ELT);
+      vreg[it] = sel16(ok, x);
+    }
+    // ---- S^T = K Q^T ------------------------------------------------------
+    f32x4 sc[C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < C::QCH; ++u) {
+        if constexpr (BF16) {
+          c = mfma_bf16(__builtin_bit_cast(bf16x8, kop[kb][u]), __builtin_bit_cast(bf16x8, qop[u]), c);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            c = mfma_f32(__uint_as_float(kop[kb][u][e]), __uint_as_float(qop[u][e]), c);
+        }
+      }
+      sc[kb] = c;
+    }
+    // ---- V chunk to LDS ---------------------------------------------------
+#pragma unroll
+    for (int it = 0; it < C::VLOADS; ++it) {
+      const int piece = it * 64 + lane;
+      const int row = piece / C::CPR;
+      const int chunk = piece - row * C::CPR;
+      lds_st16(vl, v_off<BF16, DP>(row, chunk), vreg[it]);
+    }
+    // ---- visibility + online softmax --------------------------------------
+    float mloc = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = base + 16 * kb + 4 * qg + r;
+        bool vis = key < k_end;
+        if constexpr (MASKED) vis = vis && (mrow[min(key, klast)] != 0);
+        const float x = vis ? sc[kb][r] : kNegInf;
+        sc[kb][r] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    }
+    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float msl = m_use * sl;
+    const float alpha = exp2_hw(m_run * sl - msl);
+    m_run = m_new;
+    float p[C::NKB][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = exp2_hw(fmaf(sc[kb][r], sl, -msl));
+        psum += p[kb][r];
+      }
+    }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) acc[i] *= alpha;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- O^T += V^T P^T ---------------------------------------------------
+    if constexpr (BF16) {
+#pragma unroll
+      for (int c = 0; c < C::NKB / 2; ++c) {
+        float pp[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
+                       p[2 * c + 1][0], p[2 * c + 1][1], p[2 * c + 1][2], p[2 * c + 1][3]};
+        const bf16x8 bop = to_bf16x8(pp);
+        const int row_a = 32 * c + 4 * qg + (c16 >> 2);
+        const int row_b = row_a + 16;
+        const int within = (c16 & 1) << 3;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const int chunk = 2 * db + ((c16 & 3) >> 1);
+          const i16x4 ta = lds_ld_tr16(vl, v_off<BF16, DP>(row_a, chunk) + within);
+          const i16x4 tb = lds_ld_tr16(vl, v_off<BF16, DP>(row_b, chunk) + within);
+          acc[db] = mfma_bf16(concat_bf16(ta, tb), bop, acc[db]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * kb + 4 * qg + r;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const float vv = lds_ldf(vl, row * C::ROWB + (16 * db + c16) * 4);
+            acc[db] = mfma_f32(vv, p[kb][r], acc[db]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the four waves through LDS -----------------------------------
+  float l_tot = l_run + shfl_xor_f(l_run, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  __syncthreads();  // all waves are done with their V areas
+  float* cacc = reinterpret_cast<float*>(smem_raw);              // [4][16][DP]
+  float* cm = cacc + kWaves * 16 * DP;                           // [4][16]
+  float* cl = cm + kWaves * 16;                                  // [4][16]
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    float* dst = cacc + (w * 16 + c16) * DP + 16 * db + 4 * qg;
+    *reinterpret_cast<f32x4*>(dst) = acc[db];
+  }
+  if (qg == 0) {
+    cm[w * 16 + c16] = m_run;
+    cl[w * 16 + c16] = l_tot;
+  }
+  __syncthreads();
+
+  const int ne = gh * D;
+  const bool single = (a.splits == 1);
+  float* part = single ? nullptr
+                       : a.partials + ((size_t)unit * a.splits + s) * 16 * (size_t)(D + 2);
+  for (int idx = tid; idx < ne; idx += kThreads) {
+    const int hh = idx / D;
+    const int d = idx - hh * D;
+    float mx = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, cm[ww * 16 + hh]);
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = exp2_hw((cm[ww * 16 + hh] - mu) * sl);
+      L = fmaf(cl[ww * 16 + hh], f, L);
+      A = fmaf(cacc[(ww * 16 + hh) * DP + d], f, A);
+    }
+    if (single) {
+      store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+    } else {
+      float* ph = part + (size_t)hh * (D + 2);
+      if (d == 0) {
+        ph[0] = mx;
+        ph[1] = L;
+      }
+      ph[2 + d] = A;
+    }
+  }
+}
+
+// Merge the per-split partials of one (batch row, KV head, head chunk):
+// m* = max_s m_s, o = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*),
+// in split order.  One workgroup per unit, one thread per output element.
+template <bool OUTF32>
+__global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
+  const int unit = blockIdx.x;
+  const int per_b = a.H_kv * a.head_chunks;
+  const int b = unit / per_b;
+  const int rem = unit - b * per_b;
+  const int j = rem / a.head_chunks;
+  const int hc = rem - j * a.head_chunks;
+  const int h0 = j * a.g + hc * 16;
+  const int gh = min(16, a.g - hc * 16);
+  const int D = a.D;
+  const float sl = kLog2e / sqrtf((float)D);
+  const float* pu = a.partials + (size_t)unit * a.splits * 16 * (size_t)(D + 2);
+  for (int idx = threadIdx.x; idx < gh * D; idx += kThreads) {
+    const int hh = idx / D;
+    const int d = idx - hh * D;
+    float mx = kNegInf;
+    for (int ss = 0; ss < a.splits; ++ss) mx = fmaxf(mx, pu[((size_t)ss * 16 + hh) * (D + 2)]);
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+    float L = 0.f, A = 0.f;
+    for (int ss = 0; ss < a.splits; ++ss) {
+      const float* ph = pu + ((size_t)ss * 16 + hh) * (D + 2);
+      const float f = exp2_hw((ph[0] - mu) * sl);
+      L = fmaf(ph[1], f, L);
+      A = fmaf(ph[2 + d], f, A);
+    }
+    store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+  }
+}
+
+template <bool BF16, int DP, bool EXACT, bool OUTF32>
+hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
+  const int units = a.B * a.H_kv * a.head_chunks;
+  if (a.mask) {
+    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, true, OUTF32>), dim3(units, a.splits),
+                       dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, OUTF32>), dim3(units, a.splits),
+                       dim3(kThreads), 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<OUTF32>), dim3(units), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int DP, bool OUTF32>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  return a.D == DP ? launch_dp<BF16, DP, true, OUTF32>(a, stream)
+                   : launch_dp<BF16, DP, false, OUTF32>(a, stream);
+}
+
+template <bool BF16, bool OUTF32>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (!BF16) {
+    if (a.D <= 16) return launch_d<BF16, 16, OUTF32>(a, stream);
+  }
+  if (a.D <= 32) return launch_d<BF16, 32, OUTF32>(a, stream);
+  if (a.D <= 64) return launch_d<BF16, 64, OUTF32>(a, stream);
+  if (a.D <= 128) return launch_d<BF16, 128, OUTF32>(a, stream);
+  return launch_d<BF16, 256, OUTF32>(a, stream);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int H, int H_kv, int M, int D) {
+  DecodePlan p{};
+  const int g = H / H_kv;
+  p.head_chunks = (g + 15) / 16;
+  const long units = (long)B * H_kv * p.head_chunks;
+  const long target_wgs = GQA_DECODE_TARGET_WGS;
+  const long max_splits = (M + kRoundKeys - 1) / kRoundKeys;
+  long splits = (target_wgs + units - 1) / units;
+  if (splits > max_splits) splits = max_splits;
+  if (splits > 65535) splits = 65535;
+  if (splits < 1) splits = 1;
+  long kps = (M + splits - 1) / splits;
+  kps = (kps + kRoundKeys - 1) / kRoundKeys * kRoundKeys;
+  splits = (M + kps - 1) / kps;
+  p.splits = (int)splits;
+  p.keys_per_split = (int)kps;
+  if (p.splits > 1) {
+    p.partials_bytes = (size_t)units * p.splits * 16 * (size_t)(D + 2) * 4;
+    p.workspace_bytes = p.partials_bytes;
+  }
+  return p;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.in_bf16) {
+    return a.out_f32 ? launch_t<true, true>(a, stream) : launch_t<true, false>(a, stream);
+  }
+  return launch_t<false, true>(a, stream);
+}
+
+}  // namespace gqa

@@ -1,0 +1,140 @@
+// C ABI of libgqa.so: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before any HIP call, so a rejected call has
+// no side effect.  The declarations and their contract live in include/gqa.h.
+#include "../../include/gqa.h"
+#include "gqa_internal.h"
+
+#include <limits.h>
+
+#include <initializer_list>
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t dtype_size(gqa_dtype_t t) { return t == GQA_BF16 ? 2 : 4; }
+
+bool dtype_ok(gqa_dtype_t t) { return t == GQA_F32 || t == GQA_BF16; }
+
+// [lo, lo + n) overlaps [p, p + m)?
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Product of non-negative factors, or -1 on int64 overflow.
+long long mul_checked(std::initializer_list<long long> xs) {
+  long long r = 1;
+  for (long long x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && r > LLONG_MAX / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+gqa_status_t check_common(const void* q, const void* k, const void* v, const void* out, int B,
+                          int H, int H_kv, int N, int M, int D, gqa_dtype_t in_dtype,
+                          gqa_dtype_t out_dtype) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return GQA_ERR_NULL;
+  if (B < 1 || H < 1 || H_kv < 1 || N < 1 || M < 1 || D < 1) return GQA_ERR_SHAPE;
+  if (H % H_kv != 0) return GQA_ERR_GROUP;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_DTYPE;
+  if (out_dtype != in_dtype && out_dtype != GQA_F32) return GQA_ERR_DTYPE;
+  if (D > 256 || (D * dtype_size(in_dtype)) % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  // row counts must stay below 2^31 and element counts within int64
+  const long long qrows = mul_checked({B, H, N});
+  const long long kvrows = mul_checked({B, H_kv, M});
+  const long long mask_elems = mul_checked({B, N, M});
+  if (qrows < 0 || kvrows < 0 || mask_elems < 0 || qrows >= INT_MAX || kvrows >= INT_MAX)
+    return GQA_ERR_SHAPE;
+  if (mul_checked({qrows, D, 4}) < 0 || mul_checked({kvrows, D, 4}) < 0) return GQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(gqa_status_t s) {
+  switch (s) {
+    case GQA_OK: return "success";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid shape (a dimension < 1, or sizes exceed the limits)";
+    case GQA_ERR_GROUP: return "H is not a multiple of H_kv";
+    case GQA_ERR_DTYPE: return "unsupported dtype combination";
+    case GQA_ERR_ALIGN: return "q/k/v/out/workspace must be 16-byte aligned";
+    case GQA_ERR_UNSUPPORTED: return "unsupported head_dim (need D <= 256 and D*sizeof(dtype) % 16 == 0)";
+    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    case GQA_ERR_ALIAS: return "out overlaps an input or the workspace";
+  }
+  return "unknown status";
+}
+
+size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D) {
+  if (B < 1 || H < 1 || H_kv < 1 || M < 1 || D < 1 || H % H_kv != 0) return 0;
+  const long long kvrows = mul_checked({B, H_kv, M});
+  if (kvrows < 0 || kvrows >= INT_MAX || mul_checked({B, H}) >= INT_MAX) return 0;
+  return gqa::plan_decode(B, H, H_kv, M, D).workspace_bytes;
+}
+
+gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8_t* mask,
+                        void* out, int B, int H, int H_kv, int M, int D, gqa_dtype_t in_dtype,
+                        gqa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D);
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GQA_ERR_ALIGN;
+  }
+  const size_t ein = dtype_size(in_dtype), eout = dtype_size(out_dtype);
+  const size_t qb = (size_t)B * H * D * ein, kvb = (size_t)B * H_kv * M * D * ein;
+  const size_t ob = (size_t)B * H * D * eout;
+  if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kvb) || overlaps(out, ob, v, kvb) ||
+      overlaps(out, ob, mask, (size_t)B * M) ||
+      (plan.workspace_bytes > 0 && overlaps(out, ob, workspace, plan.workspace_bytes)))
+    return GQA_ERR_ALIAS;
+
+  gqa::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
+  a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
+  a.g = H / H_kv;
+  a.head_chunks = plan.head_chunks;
+  a.splits = plan.splits;
+  a.keys_per_split = plan.keys_per_split;
+  a.in_bf16 = in_dtype == GQA_BF16;
+  a.out_f32 = out_dtype == GQA_F32;
+  if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
+  if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, const uint8_t* mask,
+                         int causal, void* out, int B, int H, int H_kv, int N, int M, int D,
+                         gqa_dtype_t in_dtype, gqa_dtype_t out_dtype, void* stream) {
+  gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, N, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  const size_t ein = dtype_size(in_dtype), eout = dtype_size(out_dtype);
+  const size_t qb = (size_t)B * H * N * D * ein, kvb = (size_t)B * H_kv * M * D * ein;
+  const size_t ob = (size_t)B * H * N * D * eout;
+  if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kvb) || overlaps(out, ob, v, kvb) ||
+      overlaps(out, ob, mask, (size_t)B * N * M))
+    return GQA_ERR_ALIAS;
+
+  gqa::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
+  a.B = B; a.H = H; a.H_kv = H_kv; a.N = N; a.M = M; a.D = D;
+  a.g = H / H_kv;
+  a.causal = causal != 0;
+  a.in_bf16 = in_dtype == GQA_BF16;
+  a.out_f32 = out_dtype == GQA_F32;
+  if (gqa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side helpers shared by the decode and prefill kernels (gfx950).
+//
+// MFMA lane layouts used throughout (wave64, checked on the hardware):
+//   v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16)+s] and
+//     B[8*(l/16)+s][l%16] for s = 0..7; the result lane l, register r holds
+//     C[4*(l/16)+r][l%16].
+//   v_mfma_f32_16x16x4f32: lane l holds A[l%16][l/16] and B[l/16][l%16];
+//     the result uses the same C layout.
+// Both attention products are formed transposed, S^T = K Q^T and
+// O^T = V^T P^T, so a lane always owns one query (or one query head) in the
+// column index l%16 and four consecutive keys (or d) in its registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Hardware 2^x (v_exp_f32).  exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 (stored as raw 16-bit) to fp32: the bf16 bits are the high half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Eight fp32 values -> one bf16x8 MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
+  u32x4 w;
+  w[0] = pack_bf16x2(x[0], x[1]);
+  w[1] = pack_bf16x2(x[2], x[3]);
+  w[2] = pack_bf16x2(x[4], x[5]);
+  w[3] = pack_bf16x2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// 16-byte global load (caller guarantees 16-byte alignment).
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ u32x4 sel16(bool keep, u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = keep ? v[i] : 0u;
+  return r;
+}
+
+// LDS accessors on a byte offset into a shared buffer.
+__device__ __forceinline__ void lds_st16(lds_char* base, uint32_t off, u32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ u32x4 lds_ld16(const lds_char* base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
+}
+__device__ __forceinline__ float lds_ldf(const lds_char* base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(base + off);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// the 16 eight-byte addresses are taken as a 4 x 16 block of 16-bit values
+// (lanes 4r..4r+3 address row r, columns 4*(lane%4)..+3); lane c of the
+// group receives column c, rows 0..3.
+__device__ __forceinline__ i16x4 lds_ld_tr16(lds_char* base, uint32_t off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+}
+
+__device__ __forceinline__ bf16x8 concat_bf16(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Cross-lane reductions inside a wave.
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace gqa

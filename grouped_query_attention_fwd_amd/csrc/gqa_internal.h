@@ -1,0 +1,55 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Arguments after validation.  Sizes are the caller's; derived values
+// (group size, padded head dim, split count) are filled by the ABI layer.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* mask;  // [B, 1, M] or null
+  void* out;
+  float* partials;      // [units][splits][16][D + 2] fp32, or null when splits == 1
+  int B, H, H_kv, M, D;
+  int g;                // H / H_kv
+  int head_chunks;      // ceil(g / 16)
+  int splits;           // key-range splits per unit
+  int keys_per_split;   // multiple of 256
+  bool in_bf16;
+  bool out_f32;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* mask;  // [B, N, M] or null
+  void* out;
+  int B, H, H_kv, N, M, D;
+  int g;
+  bool causal;
+  bool in_bf16;
+  bool out_f32;
+};
+
+// Split plan shared by the workspace query and the decode launch, so both
+// agree for the same shapes.
+struct DecodePlan {
+  int head_chunks;
+  int splits;
+  int keys_per_split;
+  size_t partials_bytes;
+  size_t workspace_bytes;  // 0 when splits == 1
+};
+DecodePlan plan_decode(int B, int H, int H_kv, int M, int D);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace gqa

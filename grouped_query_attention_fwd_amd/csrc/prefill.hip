@@ -1,0 +1,395 @@
+// Prefill (N query positions) grouped-query attention forward for gfx950.
+//
+// Operation: for each batch row b, query head h and position i,
+//   o[b,h,i,:] = softmax_{j visible}(q[b,h,i,:] . k[b,h/g,j,:] / sqrt(D)) v[b,h/g,j,:]
+// ("28. Grouped-Query Attention (GQA)", *Reference solution*: repeat-
+// interleave grouping, 1/sqrt(D) scale, [B,N,M] mask broadcast over heads;
+// "Grouped-Query Attention Explained Simply", *Minimal implementation*: the
+// causal self-attention mask, read as key j visible to query i iff j <= i).
+//
+// Design (flash-style, dense contraction on the matrix cores):
+//   * A workgroup of four waves takes the query heads of one KV group that
+//     share a block of positions (HG heads x PB positions, HG in {4,2,1});
+//     the K/V tiles it streams are therefore read once for all of its heads
+//     (the zero head stride of "Multi-Query Attention", *Implementation*) and
+//     all heads share one causal / mask frontier.
+//   * K and V tiles of BN keys are staged global -> registers -> LDS with
+//     coalesced 16-byte loads into XOR-swizzled (bf16) or padded (fp32) rows,
+//     double-buffered so the next tile's loads overlap this tile's math.
+//   * Each wave owns 16*QB query rows.  S^T = K Q^T and O^T = V^T P^T run on
+//     v_mfma_f32_16x16x32_bf16 (bf16 inputs) or v_mfma_f32_16x16x4f32 (fp32
+//     inputs); V^T is read with the transposing ds_read_b64_tr_b16.  P is
+//     rounded to bf16 for the bf16 product; all accumulation is fp32.
+//   * Online softmax per query row with exp2 and a scale of log2(e)/sqrt(D);
+//     a lane owns one query row per 16-row block, so its running max and
+//     rescale factor never leave the lane.
+//   * Causal: tiles past the block's last position are never visited and a
+//     wave skips tiles past its own rows; diagonal tiles mask per element.
+//     Mask: tiles with no visible pair are skipped entirely (no K/V load, no
+//     MFMA), decided by a workgroup-wide vote.
+//   * Causal blocks are dispatched heaviest first; consecutive workgroups
+//     cycle through (batch row, KV head) units, so with a unit count that is
+//     a multiple of 8 every block of one unit lands on the same XCD and its
+//     K/V stay in that XCD's L2.
+#include "gqa_device.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <bool BF16, int DP>
+struct PreCfg {
+  static constexpr int ELT = BF16 ? 2 : 4;
+  static constexpr int QB = (BF16 && DP <= 128) ? 2 : 1;   // 16-row query blocks per wave
+  static constexpr int RW = 16 * QB;                       // query rows per wave
+  static constexpr int BN = BF16 ? 64 : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
+  static constexpr int NKB = BN / 16;
+  static constexpr int NDB = DP / 16;
+  static constexpr int QCH = BF16 ? DP / 32 : DP / 16;     // 16-byte operand chunks per lane
+  static constexpr int CPR = DP * ELT / 16;                // 16-byte chunks per row
+  static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16; // LDS row stride
+  static constexpr int TILE = BN * ROWB;                   // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;                   // K + V
+  static constexpr int LDS_BYTES = 2 * STAGE;              // double buffered
+  static constexpr int PIECES = 2 * BN * CPR;              // 16-byte pieces per stage
+  static constexpr int PPT = PIECES / kThreads;            // pieces per thread
+  static constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;   // K row swizzle mask
+  static constexpr int SPR = DP / 16;                      // 32-byte segments per bf16 row
+  static constexpr int VSWZ = (SPR < 8 ? SPR : 8) - 1;     // V row swizzle mask
+  static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
+};
+
+template <bool BF16, int DP>
+__device__ __forceinline__ uint32_t k_off(int row, int chunk) {
+  using C = PreCfg<BF16, DP>;
+  if constexpr (BF16) return row * C::ROWB + ((chunk ^ (row & C::KSWZ)) << 4);
+  else return row * C::ROWB + (chunk << 4);
+}
+
+template <bool BF16, int DP>
+__device__ __forceinline__ uint32_t v_off(int row, int chunk) {
+  using C = PreCfg<BF16, DP>;
+  if constexpr (BF16) return row * C::ROWB + ((chunk ^ (2 * (row & C::VSWZ))) << 4);
+  else return row * C::ROWB + (chunk << 4);
+}
+
+struct Geo {
+  int b, h0, HG, PB, p0;
+};
+
+template <bool BF16, int DP, bool OUTF32>
+__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int HG, int units, int npb) {
+  using C = PreCfg<BF16, DP>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c16 = lane & 15;
+  const int qg = lane >> 4;
+
+  const int D = a.D, N = a.N, M = a.M;
+  const int groups_per_kv = a.g / HG;
+  const int L = blockIdx.x;
+  const int unit = L % units;
+  const int pbi = L / units;
+  const int pblk = a.causal ? (npb - 1 - pbi) : pbi;
+  const int b = unit / (a.H_kv * groups_per_kv);
+  const int rem = unit - b * (a.H_kv * groups_per_kv);
+  const int j = rem / groups_per_kv;
+  const int hgi = rem - j * groups_per_kv;
+  const int wph = kWaves / HG;        // waves per head
+  const int PB = wph * C::RW;         // positions per workgroup
+  const int p0 = pblk * PB;
+  const int h = j * a.g + hgi * HG + (w % HG);
+  const int wp0 = p0 + (w / HG) * C::RW;  // this wave's first position
+
+  const size_t kv_base = ((size_t)b * a.H_kv + j) * (size_t)M * D;
+  const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
+  const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
+  const uint8_t* mb = a.mask ? a.mask + (size_t)b * N * M : nullptr;
+  const float sl = kLog2e / sqrtf((float)D);
+
+  // key range of the workgroup and of this wave
+  const int last_pos = min(N, p0 + PB);          // exclusive
+  const int kend = a.causal ? min(M, last_pos) : M;
+  const int ntiles = (kend + C::BN - 1) / C::BN;
+  const int w_last = min(N, wp0 + C::RW);        // exclusive
+  const int w_kend = (wp0 >= N) ? 0 : (a.causal ? min(M, w_last) : M);
+
+  // Q operands for this wave's rows
+  u32x4 qop[C::QB][C::QCH];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int pos = wp0 + 16 * qb + c16;
+    const bool pv = pos < N;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((size_t)b * a.H + h) * N + (pv ? pos : 0)) * (size_t)D * C::ELT;
+#pragma unroll
+    for (int u = 0; u < C::QCH; ++u) {
+      const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qop[qb][u] = (pv && d0 < D) ? ld16(qp + (size_t)d0 * C::ELT) : z;
+    }
+  }
+
+  float m_run[C::QB], l_run[C::QB];
+  f32x4 acc[C::QB][C::NDB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < C::NDB; ++i) acc[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Workgroup vote: does tile t hold any visible (position, key) pair?
+  auto tile_visible = [&](int t) -> bool {
+    int any = 0;
+    const int k0 = t * C::BN;
+    for (int idx = tid; idx < PB * C::BN; idx += kThreads) {
+      const int i = idx / C::BN;
+      const int key = k0 + (idx - i * C::BN);
+      const int pos = p0 + i;
+      if (pos < N && key < kend && (!a.causal || key <= pos) && mb[(size_t)pos * M + key]) any = 1;
+    }
+    return __syncthreads_or(any) != 0;
+  };
+  auto next_tile = [&](int t) -> int {
+    if (mb == nullptr) return t;
+    while (t < ntiles && !tile_visible(t)) ++t;
+    return t;
+  };
+
+  u32x4 stage[C::PPT];
+  auto load_stage = [&](int t) {
+    const int k0 = t * C::BN;
+#pragma unroll
+    for (int it = 0; it < C::PPT; ++it) {
+      const int piece = it * kThreads + tid;
+      const int which = piece / (C::BN * C::CPR);      // 0 = K, 1 = V
+      const int rr = piece - which * (C::BN * C::CPR);
+      const int row = rr / C::CPR;
+      const int chunk = rr - row * C::CPR;
+      const int key = k0 + row;
+      const int d0 = chunk * (16 / C::ELT);
+      const char* src = which ? vp : kp;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      stage[it] = (key < M && d0 < D) ? ld16(src + ((size_t)key * D + d0) * C::ELT) : z;
+    }
+  };
+  auto store_stage = [&](int buf) {
+    lds_char* sb = smem + buf * C::STAGE;
+#pragma unroll
+    for (int it = 0; it < C::PPT; ++it) {
+      const int piece = it * kThreads + tid;
+      const int which = piece / (C::BN * C::CPR);
+      const int rr = piece - which * (C::BN * C::CPR);
+      const int row = rr / C::CPR;
+      const int chunk = rr - row * C::CPR;
+      const uint32_t off = which ? (C::TILE + v_off<BF16, DP>(row, chunk)) : k_off<BF16, DP>(row, chunk);
+      lds_st16(sb, off, stage[it]);
+    }
+  };
+
+  int t = next_tile(0);
+  if (t < ntiles) {
+    load_stage(t);
+    store_stage(0);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (t < ntiles) {
+    const int tn = next_tile(t + 1);
+    if (tn < ntiles) load_stage(tn);
+
+    const int k0 = t * C::BN;
+    if (k0 < w_kend) {
+      lds_char* kb_lds = smem + cur * C::STAGE;
+      lds_char* vb_lds = kb_lds + C::TILE;
+      // ---- S^T = K Q^T --------------------------------------------------
+      f32x4 sc[C::QB][C::NKB];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) sc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < C::QCH; ++u) {
+          const u32x4 kop = lds_ld16(kb_lds, k_off<BF16, DP>(16 * kb + c16, 4 * u + qg));
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) {
+            if constexpr (BF16) {
+              sc[qb][kb] = mfma_bf16(__builtin_bit_cast(bf16x8, kop),
+                                     __builtin_bit_cast(bf16x8, qop[qb][u]), sc[qb][kb]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sc[qb][kb] = mfma_f32(__uint_as_float(kop[e]), __uint_as_float(qop[qb][u][e]), sc[qb][kb]);
+            }
+          }
+        }
+      }
+      // ---- visibility ---------------------------------------------------
+      const bool need_mask = (mb != nullptr) || (k0 + C::BN > M) ||
+                             (a.causal && k0 + C::BN - 1 > wp0);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          const int pos = wp0 + 16 * qb + c16;
+          const bool pv = pos < N;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = k0 + 16 * kb + 4 * qg + r;
+              bool vis = pv && key < M && (!a.causal || key <= pos);
+              if (mb) vis = vis && (mb[(size_t)(pv ? pos : 0) * M + (key < M ? key : 0)] != 0);
+              if (!vis) sc[qb][kb][r] = kNegInf;
+            }
+          }
+        }
+      }
+      // ---- online softmax -----------------------------------------------
+      bf16x8 bop[C::QB][C::NKB / 2 > 0 ? C::NKB / 2 : 1];
+      float pf[C::QB][C::NKB][4];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float mloc = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[qb][kb][r]);
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+        const float m_new = fmaxf(m_run[qb], mloc);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float msl = m_use * sl;
+        const float alpha = exp2_hw(m_run[qb] * sl - msl);
+        m_run[qb] = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pf[qb][kb][r] = exp2_hw(fmaf(sc[qb][kb][r], sl, -msl));
+            psum += pf[qb][kb][r];
+          }
+        l_run[qb] = fmaf(l_run[qb], alpha, psum);
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) acc[qb][i] *= alpha;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int c = 0; c < C::NKB / 2; ++c) {
+            float pp[8] = {pf[qb][2 * c][0], pf[qb][2 * c][1], pf[qb][2 * c][2], pf[qb][2 * c][3],
+                           pf[qb][2 * c + 1][0], pf[qb][2 * c + 1][1], pf[qb][2 * c + 1][2],
+                           pf[qb][2 * c + 1][3]};
+            bop[qb][c] = to_bf16x8(pp);
+          }
+        }
+      }
+      // ---- O^T += V^T P^T -----------------------------------------------
+      if constexpr (BF16) {
+#pragma unroll
+        for (int c = 0; c < C::NKB / 2; ++c) {
+          const int row_a = 32 * c + 4 * qg + (c16 >> 2);
+          const int row_b = row_a + 16;
+          const int within = (c16 & 1) << 3;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const int chunk = 2 * db + ((c16 & 3) >> 1);
+            const i16x4 ta = lds_ld_tr16(vb_lds, v_off<BF16, DP>(row_a, chunk) + within);
+            const i16x4 tb = lds_ld_tr16(vb_lds, v_off<BF16, DP>(row_b, chunk) + within);
+            const bf16x8 vop = concat_bf16(ta, tb);
+#pragma unroll
+            for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_bf16(vop, bop[qb][c], acc[qb][db]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * kb + 4 * qg + r;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+              const float vv = lds_ldf(vb_lds, row * C::ROWB + (16 * db + c16) * 4);
+#pragma unroll
+              for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_f32(vv, pf[qb][kb][r], acc[qb][db]);
+            }
+          }
+      }
+    }
+
+    if (tn < ntiles) store_stage(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    t = tn;
+  }
+
+  // ---- epilogue: O = acc / l ------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float lt = l_run[qb] + shfl_xor_f(l_run[qb], 16);
+    lt += shfl_xor_f(lt, 32);
+    const int pos = wp0 + 16 * qb + c16;
+    if (pos >= N) continue;
+    const size_t obase = (((size_t)b * a.H + h) * N + pos) * (size_t)D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = 16 * db + 4 * qg;
+      if (d >= D) continue;
+      // a true division (not a reciprocal multiply) keeps l*x/l == x exact;
+      // a row with no visible key has l == 0 and acc == 0, giving NaN
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = acc[qb][db][e] / lt;
+      if constexpr (OUTF32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + d) = o;
+      } else {
+        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d) = pk;
+      }
+    }
+  }
+}
+
+template <bool BF16, int DP, bool OUTF32>
+hipError_t launch_dp(const PrefillArgs& a, hipStream_t stream) {
+  using C = PreCfg<BF16, DP>;
+  const int HG = (a.g % 4 == 0) ? 4 : ((a.g % 2 == 0) ? 2 : 1);
+  const int PB = (kWaves / HG) * C::RW;
+  const int npb = (a.N + PB - 1) / PB;
+  const int units = a.B * a.H_kv * (a.g / HG);
+  const long blocks = (long)npb * units;
+  hipLaunchKernelGGL((prefill_kernel<BF16, DP, OUTF32>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, a, HG, units, npb);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool OUTF32>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  if constexpr (!BF16) {
+    if (a.D <= 16) return launch_dp<BF16, 16, OUTF32>(a, stream);
+  }
+  if (a.D <= 32) return launch_dp<BF16, 32, OUTF32>(a, stream);
+  if (a.D <= 64) return launch_dp<BF16, 64, OUTF32>(a, stream);
+  if (a.D <= 128) return launch_dp<BF16, 128, OUTF32>(a, stream);
+  return launch_dp<BF16, 256, OUTF32>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.in_bf16) {
+    return a.out_f32 ? launch_t<true, true>(a, stream) : launch_t<true, false>(a, stream);
+  }
+  return launch_t<false, true>(a, stream);
+}
+
+}  // namespace gqa

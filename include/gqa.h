@@ -1,0 +1,136 @@
+/*
+ * gqa.h - C ABI of the grouped-query attention forward library (libgqa.so),
+ * built for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (all entry points): for every batch row b, query head h and
+ * query position i,
+ *
+ *     O[b,h,i,:] = sum_j softmax_j( Q[b,h,i,:] . K[b,h/g,j,:] / sqrt(D) ) V[b,h/g,j,:]
+ *
+ * with g = H / H_kv query heads per KV head, i.e. query head h reads KV head
+ * h / g (integer division).  That is the repeat-interleave grouping of
+ * "28. Grouped-Query Attention (GQA)" (sections *Problem*, *Step-by-Step
+ * Approach*, *Reference solution*) and the [B,H,N,D] / [B,H_kv,M,D] interface
+ * of "Multi-Query Attention" (section *Implementation*), where a real kernel
+ * expresses the grouping as a zero stride over the head dimension instead of
+ * materialising the expansion.  The group size comes from the shapes; there is
+ * no separate group argument.
+ *
+ * The softmax runs over the keys that are visible to query i:
+ *   - mask (optional, may be NULL): uint8 [B, N, M], nonzero = key visible,
+ *     the same for every head (the reference solution's boolean mask, which
+ *     is broadcast over heads and sets invisible scores to -inf);
+ *   - causal (prefill only): key j visible to query i iff j <= i, for any N
+ *     and M (top-left aligned; the self-attention causal mask of "Grouped-Query
+ *     Attention Explained Simply", *Minimal implementation*).
+ *   Mask and causal combine by AND.  A query row that sees no key yields NaN
+ *   in every output element of that row (the reference recipe's softmax over
+ *   all -inf scores).
+ *
+ * Layouts: contiguous row-major.  q [B,H,N,D], k and v [B,H_kv,M,D],
+ * out [B,H,N,D].  Scale is fixed at 1/sqrt(D).  Accumulation is fp32.
+ *
+ * Supported: all dims >= 1, H % H_kv == 0, 1 <= D <= 256,
+ * D * sizeof(in_dtype) a multiple of 16 bytes (bf16: D % 8 == 0; fp32:
+ * D % 4 == 0).  q, k, v, out and workspace must be 16-byte aligned.
+ * in_dtype is the type of q, k and v; out_dtype is in_dtype or GQA_F32.
+ * Element counts must fit in a signed 64-bit integer and B*H*N, B*H_kv*M
+ * must each stay below 2^31 rows.
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The
+ * library never allocates, frees or keeps a pointer past the call.  out must
+ * not overlap q, k, v, mask or workspace.
+ *
+ * Synchronisation and errors: calls are asynchronous.  They return after
+ * enqueueing work on `stream` (a hipStream_t passed as void*; NULL is the
+ * default stream).  Every argument check runs on the host before any HIP call,
+ * so a rejected call has no side effect.  The library never aborts and never
+ * prints.  Calls on different streams are independent as long as each decode
+ * call uses its own workspace.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  GQA_ERR_SHAPE = 2,       /* a dimension < 1, or sizes overflow the limits   */
+  GQA_ERR_GROUP = 3,       /* H is not a multiple of H_kv                     */
+  GQA_ERR_DTYPE = 4,       /* unknown dtype, or out_dtype not in {in, F32}    */
+  GQA_ERR_ALIGN = 5,       /* q/k/v/out/workspace not 16-byte aligned         */
+  GQA_ERR_UNSUPPORTED = 6, /* D > 256 or D*sizeof(in_dtype) % 16 != 0         */
+  GQA_ERR_WORKSPACE = 7,   /* decode workspace missing or too small           */
+  GQA_ERR_HIP = 8,         /* the HIP runtime reported a launch error         */
+  GQA_ERR_ALIAS = 9        /* out overlaps an input or the workspace          */
+} gqa_status_t;
+
+typedef enum {
+  GQA_F32 = 0,  /* IEEE binary32                                              */
+  GQA_BF16 = 1  /* bfloat16; outputs are rounded to nearest, ties to even     */
+} gqa_dtype_t;
+
+/*
+ * Decode: one query position per (batch row, head), N = 1.  This is the
+ * autoregressive step that re-reads the whole KV cache (the bandwidth-bound
+ * case of "Multi-Query Attention", *Theory*; "Grouped-Query Attention
+ * Explained Simply", Q/A on why decode is memory-bandwidth bound).
+ *
+ *   q    [B, H, 1, D]     in_dtype
+ *   k, v [B, H_kv, M, D]  in_dtype (the KV cache, M cached positions)
+ *   mask [B, 1, M] uint8 or NULL (nonzero = key visible)
+ *   out  [B, H, 1, D]     out_dtype
+ *   workspace: device buffer of at least gqa_decode_workspace_size(...)
+ *     bytes (may be NULL when that size is 0).  It holds per-split fp32
+ *     partial results between the two kernels of the call; its contents need
+ *     no initialisation and are meaningless afterwards.  Two calls that may
+ *     run at the same time (different streams) need two workspaces.
+ * The result is deterministic: the same inputs give bit-identical outputs.
+ */
+gqa_status_t gqa_decode(const void* q, const void* k, const void* v,
+                        const uint8_t* mask, void* out,
+                        int B, int H, int H_kv, int M, int D,
+                        gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Bytes of decode workspace for these sizes (independent of dtype and of
+ * the device).  Returns 0 when no workspace is needed or when the sizes are
+ * invalid (gqa_decode then reports the size error).
+ */
+size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D);
+
+/*
+ * Prefill: N query positions per (batch row, head) against M keys, with an
+ * optional mask and causal flag (the self-attention forward of "Grouped-Query
+ * Attention Explained Simply", *Minimal implementation*, and the masked
+ * forward of the reference solution of "28. Grouped-Query Attention (GQA)").
+ *
+ *   q    [B, H, N, D]     in_dtype
+ *   k, v [B, H_kv, M, D]  in_dtype
+ *   mask [B, N, M] uint8 or NULL (nonzero = key visible)
+ *   causal: 0 or 1 (nonzero): key j visible to query i iff j <= i
+ *   out  [B, H, N, D]     out_dtype
+ * No workspace.  Deterministic.
+ */
+gqa_status_t gqa_prefill(const void* q, const void* k, const void* v,
+                         const uint8_t* mask, int causal, void* out,
+                         int B, int H, int H_kv, int N, int M, int D,
+                         gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
+                         void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gqa_status_string(gqa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -1,0 +1,125 @@
+"""C ABI on the CPU: the library loads, exports every entry point the header
+declares (and nothing else), and rejects every invalid call before any HIP
+call is made (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import grouped_query_attention_fwd_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, NULL, SHAPE, GROUP, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(10)
+F32, BF16 = 0, 1
+
+# fake, 16-byte aligned, non-overlapping "device" addresses: never dereferenced
+# because every call below fails validation first
+Q, K, V, O, W, MK = (0x10000000 * (i + 1) for i in range(6))
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gqa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.load_library()
+
+
+def test_exports_match_header(lib):
+    names = declared_functions()
+    assert names == ["gqa_decode", "gqa_decode_workspace_size", "gqa_prefill",
+                     "gqa_status_string"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gqa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines()
+                      if " T " in line)
+    assert exported == names
+
+
+def test_status_strings(lib):
+    for code in range(10):
+        s = gqa.status_string(code)
+        assert s and s != "unknown status"
+    assert gqa.status_string(123) == "unknown status"
+
+
+def dec(lib, q=Q, k=K, v=V, mask=None, out=O, B=2, H=8, H_kv=2, M=300, D=128,
+        tin=BF16, tout=BF16, ws=W, wsb=1 << 30):
+    return lib.gqa_decode(q, k, v, mask, out, B, H, H_kv, M, D, tin, tout, ws, wsb, None)
+
+
+def pre(lib, q=Q, k=K, v=V, mask=None, causal=0, out=O, B=2, H=8, H_kv=2, N=7, M=9,
+        D=128, tin=BF16, tout=BF16):
+    return lib.gqa_prefill(q, k, v, mask, causal, out, B, H, H_kv, N, M, D, tin, tout, None)
+
+
+@pytest.mark.parametrize("fn", [dec, pre])
+def test_rejections_common(lib, fn):
+    assert fn(lib, q=None) == NULL
+    assert fn(lib, k=None) == NULL
+    assert fn(lib, v=None) == NULL
+    assert fn(lib, out=None) == NULL
+    assert fn(lib, B=0) == SHAPE
+    assert fn(lib, H=0) == SHAPE
+    assert fn(lib, H_kv=0) == SHAPE
+    assert fn(lib, M=0) == SHAPE
+    assert fn(lib, D=0) == SHAPE
+    assert fn(lib, B=-3) == SHAPE
+    assert fn(lib, H=6, H_kv=4) == GROUP
+    assert fn(lib, tin=7) == DTYPE
+    assert fn(lib, tout=9) == DTYPE
+    assert fn(lib, tin=F32, tout=BF16, D=128) == DTYPE   # fp32 in, bf16 out
+    assert fn(lib, D=264) == UNSUP
+    assert fn(lib, D=12) == UNSUP                         # bf16 needs D % 8 == 0
+    assert fn(lib, tin=F32, tout=F32, D=6) == UNSUP       # fp32 needs D % 4 == 0
+    assert fn(lib, q=Q + 8) == ALIGN
+    assert fn(lib, k=K + 2) == ALIGN
+    assert fn(lib, out=O + 4) == ALIGN
+    assert fn(lib, out=Q) == ALIAS
+    assert fn(lib, out=K + 16) == ALIAS
+    assert fn(lib, B=1 << 20, H=1 << 12, H_kv=1 << 12) == SHAPE  # rows >= 2^31
+
+
+def test_rejections_prefill(lib):
+    assert pre(lib, N=0) == SHAPE
+    assert pre(lib, mask=O) == ALIAS
+
+
+def test_rejections_decode_workspace(lib):
+    need = lib.gqa_decode_workspace_size(2, 8, 2, 300, 128)
+    assert need > 0
+    assert dec(lib, ws=None, wsb=0) == WS
+    assert dec(lib, wsb=need - 1) == WS
+    assert dec(lib, ws=W + 8, wsb=need) == ALIGN
+    assert dec(lib, out=W, wsb=need) == ALIAS
+
+
+def test_workspace_size_rules(lib):
+    f = lib.gqa_decode_workspace_size
+    assert f(0, 8, 2, 64, 128) == 0
+    assert f(1, 6, 4, 64, 128) == 0          # bad group
+    # many units: one split per unit, no workspace
+    assert f(512, 8, 8, 256, 128) == 0
+    # the Mistral-7B-shaped decode needs splits and therefore a workspace
+    s2 = f(16, 32, 8, 4096, 128)
+    assert s2 > 0 and s2 % 4 == 0
+    # independent of the dtype-free arguments' order of calls (pure function)
+    assert f(16, 32, 8, 4096, 128) == s2
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gqa.decode(q, q[:, :2], q[:, :2])
+    with pytest.raises(ValueError):
+        gqa.prefill(q, q[:, :2], q[:, :2])

@@ -1,0 +1,140 @@
+"""GPU parity of gqa_decode against the fp64 oracle (through the C ABI)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_attention_fwd_amd as gqa
+import workloads
+from tests.parity import TOL, compare, np64, oracle_out, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(seed, B, H, H_kv, M, D, dtype, mask_kind=None, q_scale=1.0, out_dtype=None):
+    say(f"decode case seed={seed} B={B} H={H} H_kv={H_kv} M={M} D={D} {dtype} mask={mask_kind}")
+    q, k, v, mask = workloads.random_case(seed, B, H, H_kv, 1, M, D, dtype, mask_kind, q_scale)
+    ref = oracle_out(q, k, v, mask)
+    qd, kd, vd, md = to_dev(q, k, v, mask)
+    out = gqa.decode(qd, kd, vd, md, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    return compare(out, ref, tol, f"decode seed={seed}")
+
+
+SMALL = [
+    # seed, B, H, H_kv, M, D, dtype, mask
+    (1, 2, 8, 2, 64, 128, torch.bfloat16, None),
+    (2, 3, 8, 8, 1, 64, torch.bfloat16, None),        # MHA, single key
+    (3, 2, 6, 3, 255, 32, torch.bfloat16, None),      # ragged M, g = 2
+    (4, 1, 16, 1, 1000, 128, torch.bfloat16, None),   # MQA g = 16
+    (5, 2, 40, 2, 777, 64, torch.bfloat16, None),     # g = 20: two head chunks
+    (6, 2, 64, 1, 300, 256, torch.bfloat16, None),    # g = 64, D = 256
+    (7, 4, 8, 2, 4097, 96, torch.bfloat16, None),     # D padded to 128
+    (8, 2, 4, 2, 513, 8, torch.bfloat16, None),
+    (9, 2, 4, 2, 130, 24, torch.bfloat16, None),
+    (10, 2, 8, 2, 600, 128, torch.bfloat16, "padding"),
+    (11, 2, 8, 4, 333, 128, torch.bfloat16, "random"),
+    (12, 2, 8, 2, 1100, 128, torch.bfloat16, "blocks"),
+    (20, 2, 8, 2, 64, 16, torch.float32, None),
+    (21, 2, 4, 2, 5, 4, torch.float32, None),
+    (22, 2, 12, 4, 300, 12, torch.float32, None),
+    (23, 1, 16, 2, 2000, 64, torch.float32, "padding"),
+    (24, 2, 8, 8, 257, 128, torch.float32, "random"),
+    (25, 1, 4, 1, 700, 256, torch.float32, None),
+    (26, 2, 6, 2, 1500, 36, torch.float32, "blocks"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"s{c[0]}")
+def test_decode_small(case):
+    seed, B, H, H_kv, M, D, dtype, mk = case
+    run_case(seed, B, H, H_kv, M, D, dtype, mk)
+
+
+def test_decode_peaky_scores():
+    # q scaled x4 makes one key dominate and stresses the running-max rescale
+    run_case(30, 2, 8, 2, 3000, 128, torch.bfloat16, None, q_scale=4.0)
+    run_case(31, 2, 8, 2, 3000, 64, torch.float32, None, q_scale=4.0)
+
+
+def test_decode_fp32_output_of_bf16_inputs():
+    mx, _ = run_case(32, 2, 8, 2, 1024, 128, torch.bfloat16, None, out_dtype=torch.float32)
+    assert mx < 5e-3
+
+
+def test_decode_empty_rows_are_nan():
+    B, H, H_kv, M, D = 3, 8, 2, 300, 128
+    q, k, v, _ = workloads.random_case(40, B, H, H_kv, 1, M, D, torch.bfloat16)
+    mask = torch.ones(B, 1, M, dtype=torch.bool)
+    mask[1] = False                      # batch row 1 sees nothing
+    mask[2, 0, 200:] = False
+    ref = oracle_out(q, k, v, mask)
+    assert np.isnan(ref[1]).all()
+    qd, kd, vd, md = to_dev(q, k, v, mask)
+    out = gqa.decode(qd, kd, vd, md)
+    compare(out, ref, TOL[torch.bfloat16], "empty rows")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 4096, 128), (1, 48, 3, 999, 64), (2, 4, 4, 70, 32)])
+def test_decode_head_mapping_bit_exact(dtype, shape):
+    """K = 0 and V[b, j] = j: every score is 0, every weight 1, so query head
+    h must return exactly h // g (repeat-interleave, not tiling)."""
+    B, H, H_kv, M, D = shape
+    say(f"head mapping {shape} {dtype}")
+    g = H // H_kv
+    q = torch.randn(B, H, 1, D).to(dtype)
+    k = torch.zeros(B, H_kv, M, D, dtype=dtype)
+    v = torch.arange(H_kv, dtype=torch.float32)[None, :, None, None].expand(B, H_kv, M, D)
+    v = v.contiguous().to(dtype)
+    qd, kd, vd = to_dev(q, k, v)
+    out = gqa.decode(qd, kd, vd).float().cpu()
+    want = (torch.arange(H) // g).float()[None, :, None, None].expand(B, H, 1, D)
+    assert torch.equal(out, want)
+
+
+def test_decode_deterministic_and_workspace_reuse():
+    B, H, H_kv, M, D = 4, 32, 8, 4096, 128
+    q, k, v, _ = workloads.random_case(50, B, H, H_kv, 1, M, D, torch.bfloat16)
+    qd, kd, vd = to_dev(q, k, v)
+    ws = torch.zeros(gqa.decode_workspace_size(B, H, H_kv, M, D), dtype=torch.uint8, device="cuda")
+    outs = [gqa.decode(qd, kd, vd, workspace=ws).clone() for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    # a different problem through the same workspace, then the first again
+    q2, k2, v2, _ = workloads.random_case(51, B, H, H_kv, 1, 1000, D, torch.bfloat16)
+    gqa.decode(*to_dev(q2, k2, v2), workspace=ws)
+    assert torch.equal(gqa.decode(qd, kd, vd, workspace=ws), outs[0])
+    compare(outs[0], oracle_out(q, k, v), TOL[torch.bfloat16], "reuse")
+
+
+def test_decode_mistral7b_full():
+    """Mistral-7B-shaped decode at full size, every output checked."""
+    w = workloads.by_name("decode_mistral7b_m4096")
+    q, k, v, mask, _ = workloads.make_inputs(w)
+    say("decode mistral full")
+    out = gqa.decode(*to_dev(q, k, v))
+    mx, rr = compare(out, oracle_out(q, k, v), TOL[torch.bfloat16], w.name)
+    say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")
+
+
+def test_decode_llama70b_full_sampled():
+    """Llama-2-70B-shaped decode (M = 32768) at full size, in the launch
+    configuration the benchmark times; three batch rows checked against the
+    oracle (the oracle computes them one by one)."""
+    w = workloads.by_name("decode_llama70b_m32768")
+    q, k, v, mask, _ = workloads.make_inputs(w)
+    say("decode llama70b full")
+    out = gqa.decode(*to_dev(q, k, v)).cpu()
+    for b in (0, 7, 15):
+        ref = oracle_out(q[b:b + 1], k[b:b + 1], v[b:b + 1])
+        mx, rr = compare(out[b:b + 1], ref, TOL[torch.bfloat16], f"{w.name} b={b}")
+        say(f"  b={b} max abs err {mx:.3e} rel rms {rr:.3e}")
