@@ -36,19 +36,22 @@
 namespace gqa {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef GQA_DECODE_WAVES
+#define GQA_DECODE_WAVES 4
+#endif
+constexpr int kWaves = GQA_DECODE_WAVES;  // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 // Workgroups to aim for when choosing the split count.
 #ifndef GQA_DECODE_TARGET_WGS
-#define GQA_DECODE_TARGET_WGS 512
+#define GQA_DECODE_TARGET_WGS 256
 #endif
 
 template <bool BF16, int DP>
 struct DecCfg {
   static constexpr int ELT = BF16 ? 2 : 4;
   // keys per wave chunk (bounded by LDS and by the registers of the loads)
-  static constexpr int KC = BF16 ? (DP <= 128 ? 64 : 32) : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));
+  static constexpr int KC = BF16 ? (DP <= 64 ? 64 : 32) : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));
   static constexpr int NKB = KC / 16;                 // 16-key MFMA blocks per chunk
   static constexpr int NDB = DP / 16;                 // 16-wide d blocks of O
   static constexpr int QCH = BF16 ? DP / 32 : DP / 16;  // 16-byte Q/K chunks per lane per key
@@ -58,6 +61,10 @@ struct DecCfg {
   static constexpr int VLOADS = KC * CPR / 64;        // 16-byte V loads per lane per chunk
   static constexpr int SPR = DP / 16;                 // 32-byte segments per bf16 row
   static constexpr int SWZ = (SPR < 8 ? SPR : 8) - 1;
+  // Registers of one chunk's loads; when two chunks fit, the next chunk is
+  // loaded while the current one is computed.
+  static constexpr int LOAD_VGPRS = (NKB * QCH + VLOADS) * 4;
+  static constexpr bool PREFETCH = LOAD_VGPRS <= 64;
   static constexpr int COMBINE_BYTES = kWaves * 16 * DP * 4 + 2 * kWaves * 16 * 4;
   static constexpr int LDS_BYTES =
       (kWaves * VBYTES > COMBINE_BYTES) ? kWaves * VBYTES : COMBINE_BYTES;
@@ -85,7 +92,7 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
 
 // EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is given.
 template <bool BF16, int DP, bool EXACT, bool MASKED, bool OUTF32>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs a) {
   using C = DecCfg<BF16, DP>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
   lds_char* smem = (lds_char*)smem_raw;
@@ -142,9 +149,15 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   lds_char* vl = smem + w * C::VBYTES;
   const int klast = k_end - 1;
 
-  for (int base = k_begin + w * C::KC; base < k_end; base += kWaves * C::KC) {
-    // ---- issue all loads of the chunk: K first, then V -------------------
-    u32x4 kop[C::NKB][C::QCH];
+  struct Chunk {
+    u32x4 k[C::NKB][C::QCH];  // K rows in MFMA A-operand layout
+    u32x4 v[C::VLOADS];       // V rows, coalesced 16-byte pieces
+  };
+  // Issue every load of the chunk at `base` (K first, then V).  Addresses
+  // are clamped to valid rows; rows past the split are zeroed (V) or masked
+  // to -inf later (K).
+  auto load_chunk = [&](int base) {
+    Chunk ch;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       const int key = min(base + 16 * kb + c16, klast);
@@ -153,14 +166,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       for (int u = 0; u < C::QCH; ++u) {
         const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
         if constexpr (EXACT) {
-          kop[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
+          ch.k[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
         } else {
           const bool dv = d0 < D;
-          kop[kb][u] = sel16(dv, ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT));
+          ch.k[kb][u] = sel16(dv, ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT));
         }
       }
     }
-    u32x4 vreg[C::VLOADS];
 #pragma unroll
     for (int it = 0; it < C::VLOADS; ++it) {
       const int piece = it * 64 + lane;
@@ -170,8 +182,24 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       const int d0 = chunk * (16 / C::ELT);
       const bool ok = key < k_end && (EXACT || d0 < D);
       const u32x4 x = ld16(vp + ((size_t)min(key, klast) * D + (ok ? d0 : 0)) * C::ELT);
-      vreg[it] = sel16(ok, x);
+      ch.v[it] = sel16(ok, x);
     }
+    return ch;
+  };
+
+  const int kstride = kWaves * C::KC;
+  int base = k_begin + w * C::KC;
+  Chunk cur;
+  if (base < k_end) cur = load_chunk(base);
+  while (base < k_end) {
+    const int nb = base + kstride;
+    const bool more = nb < k_end;
+    Chunk nxt;
+    if constexpr (C::PREFETCH) {
+      if (more) nxt = load_chunk(nb);
+    }
+    const auto& kop = cur.k;
+    const auto& vreg = cur.v;
     // ---- S^T = K Q^T ------------------------------------------------------
     f32x4 sc[C::NKB];
 #pragma unroll
@@ -271,9 +299,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (!more) break;
+    if constexpr (C::PREFETCH) {
+      cur = nxt;
+    } else {
+      cur = load_chunk(nb);
+    }
+    base = nb;
   }
 
-  // ---- merge the four waves through LDS -----------------------------------
+  // ---- merge the waves through LDS -----------------------------------
   float l_tot = l_run + shfl_xor_f(l_run, 16);
   l_tot += shfl_xor_f(l_tot, 32);
   __syncthreads();  // all waves are done with their V areas
@@ -324,9 +359,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 
 // Merge the per-split partials of one (batch row, KV head, head chunk):
 // m* = max_s m_s, o = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*),
-// in split order.  One workgroup per unit, one thread per output element.
+// in split order.  One thread per output element; blockIdx.y walks the
+// (head, d) elements of a unit in blocks of kMergeThreads.
+constexpr int kMergeThreads = 128;
 template <bool OUTF32>
-__global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int per_b = a.H_kv * a.head_chunks;
   const int b = unit / per_b;
@@ -336,23 +373,24 @@ __global__ void __launch_bounds__(kThreads) decode_merge_kernel(DecodeArgs a) {
   const int h0 = j * a.g + hc * 16;
   const int gh = min(16, a.g - hc * 16);
   const int D = a.D;
+  const int idx = blockIdx.y * kMergeThreads + threadIdx.x;
+  if (idx >= gh * D) return;
+  const int hh = idx / D;
+  const int d = idx - hh * D;
   const float sl = kLog2e / sqrtf((float)D);
-  const float* pu = a.partials + (size_t)unit * a.splits * 16 * (size_t)(D + 2);
-  for (int idx = threadIdx.x; idx < gh * D; idx += kThreads) {
-    const int hh = idx / D;
-    const int d = idx - hh * D;
-    float mx = kNegInf;
-    for (int ss = 0; ss < a.splits; ++ss) mx = fmaxf(mx, pu[((size_t)ss * 16 + hh) * (D + 2)]);
-    const float mu = (mx == kNegInf) ? 0.f : mx;
-    float L = 0.f, A = 0.f;
-    for (int ss = 0; ss < a.splits; ++ss) {
-      const float* ph = pu + ((size_t)ss * 16 + hh) * (D + 2);
-      const float f = exp2_hw((ph[0] - mu) * sl);
-      L = fmaf(ph[1], f, L);
-      A = fmaf(ph[2 + d], f, A);
-    }
-    store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+  const size_t stride = 16 * (size_t)(D + 2);
+  const float* ph = a.partials + (size_t)unit * a.splits * stride + (size_t)hh * (D + 2);
+  float mx = kNegInf;
+  for (int ss = 0; ss < a.splits; ++ss) mx = fmaxf(mx, ph[ss * stride]);
+  const float mu = (mx == kNegInf) ? 0.f : mx;
+  float L = 0.f, A = 0.f;
+  for (int ss = 0; ss < a.splits; ++ss) {
+    const float* p = ph + ss * stride;
+    const float f = exp2_hw((p[0] - mu) * sl);
+    L = fmaf(p[1], f, L);
+    A = fmaf(p[2 + d], f, A);
   }
+  store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
 }
 
 template <bool BF16, int DP, bool EXACT, bool OUTF32>
@@ -367,7 +405,9 @@ hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<OUTF32>), dim3(units), dim3(kThreads), 0, stream, a);
+  const int per_unit = (min(16, a.g) * a.D + kMergeThreads - 1) / kMergeThreads;
+  hipLaunchKernelGGL((decode_merge_kernel<OUTF32>), dim3(units, per_unit), dim3(kMergeThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -43,16 +43,18 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (v_cvt_pk_bf16_f32: round to nearest, ties to
+// even; NaN stays NaN).  `lo` lands in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 // Eight fp32 values -> one bf16x8 MFMA operand (round to nearest even).
@@ -82,6 +84,13 @@ __device__ __forceinline__ u32x4 sel16(bool keep, u32x4 v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = keep ? v[i] : 0u;
   return r;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
+// The LDS destination is `lds_base` + 16 * lane: `lds_base` must be the same
+// for the whole wave; each lane chooses its global source freely.
+__device__ __forceinline__ void dma16(const void* gsrc, lds_char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
 // LDS accessors on a byte offset into a shared buffer.

@@ -13,20 +13,25 @@
 //     the K/V tiles it streams are therefore read once for all of its heads
 //     (the zero head stride of "Multi-Query Attention", *Implementation*) and
 //     all heads share one causal / mask frontier.
-//   * K and V tiles of BN keys are staged global -> registers -> LDS with
-//     coalesced 16-byte loads into XOR-swizzled (bf16) or padded (fp32) rows,
-//     double-buffered so the next tile's loads overlap this tile's math.
+//   * K and V tiles of BN keys are double-buffered in LDS.  bf16 tiles whose
+//     rows need no column padding go straight from global memory to LDS with
+//     global_load_lds_dwordx4 (no staging registers); the XOR swizzle of the
+//     LDS rows is applied by permuting each lane's global source.  Other
+//     cases stage through registers.  The next tile's copy is issued before
+//     the current tile's math, so its latency hides behind the MFMAs.
 //   * Each wave owns 16*QB query rows.  S^T = K Q^T and O^T = V^T P^T run on
 //     v_mfma_f32_16x16x32_bf16 (bf16 inputs) or v_mfma_f32_16x16x4f32 (fp32
 //     inputs); V^T is read with the transposing ds_read_b64_tr_b16.  P is
-//     rounded to bf16 for the bf16 product; all accumulation is fp32.
+//     rounded to bf16 (v_cvt_pk_bf16_f32) for the bf16 product; all
+//     accumulation is fp32.
 //   * Online softmax per query row with exp2 and a scale of log2(e)/sqrt(D);
 //     a lane owns one query row per 16-row block, so its running max and
 //     rescale factor never leave the lane.
 //   * Causal: tiles past the block's last position are never visited and a
-//     wave skips tiles past its own rows; diagonal tiles mask per element.
-//     Mask: tiles with no visible pair are skipped entirely (no K/V load, no
-//     MFMA), decided by a workgroup-wide vote.
+//     wave skips tiles past its own rows; only tiles that cross the diagonal,
+//     the end of the keys or a mask pay for per-element visibility.  Mask:
+//     tiles with no visible pair are skipped entirely (no K/V copy, no MFMA),
+//     decided by a workgroup-wide vote.
 //   * Causal blocks are dispatched heaviest first; consecutive workgroups
 //     cycle through (batch row, KV head) units, so with a unit count that is
 //     a multiple of 8 every block of one unit lands on the same XCD and its
@@ -59,7 +64,11 @@ struct PreCfg {
   static constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;   // K row swizzle mask
   static constexpr int SPR = DP / 16;                      // 32-byte segments per bf16 row
   static constexpr int VSWZ = (SPR < 8 ? SPR : 8) - 1;     // V row swizzle mask
+  // direct copies: one wave instruction fills 1 KB = RPI rows of a tile
+  static constexpr int RPI = BF16 ? 1024 / ROWB : 1;
+  static constexpr int DMA_PER_TILE = BF16 ? BN / RPI / kWaves : 0;  // per wave, per K or V tile
   static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
+  static_assert(!BF16 || (BN % (RPI * kWaves) == 0), "direct copy must split evenly");
 };
 
 template <bool BF16, int DP>
@@ -76,13 +85,12 @@ __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
   else return row * C::ROWB + (chunk << 4);
 }
 
-struct Geo {
-  int b, h0, HG, PB, p0;
-};
-
-template <bool BF16, int DP, bool OUTF32>
+// DIRECT: bf16 with D == DP, tiles copied straight into LDS.
+// MASKED: a [B,N,M] mask is given.
+template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int HG, int units, int npb) {
   using C = PreCfg<BF16, DP>;
+  static_assert(!DIRECT || BF16, "direct copies are for bf16 tiles");
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
   lds_char* smem = (lds_char*)smem_raw;
 
@@ -92,12 +100,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   const int c16 = lane & 15;
   const int qg = lane >> 4;
 
-  const int D = a.D, N = a.N, M = a.M;
+  const int D = DIRECT ? DP : a.D;
+  const int N = a.N, M = a.M;
+  const bool causal = a.causal;
   const int groups_per_kv = a.g / HG;
   const int L = blockIdx.x;
   const int unit = L % units;
   const int pbi = L / units;
-  const int pblk = a.causal ? (npb - 1 - pbi) : pbi;
+  const int pblk = causal ? (npb - 1 - pbi) : pbi;
   const int b = unit / (a.H_kv * groups_per_kv);
   const int rem = unit - b * (a.H_kv * groups_per_kv);
   const int j = rem / groups_per_kv;
@@ -111,17 +121,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   const size_t kv_base = ((size_t)b * a.H_kv + j) * (size_t)M * D;
   const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
   const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
-  const uint8_t* mb = a.mask ? a.mask + (size_t)b * N * M : nullptr;
+  const uint8_t* mb = MASKED ? a.mask + (size_t)b * N * M : nullptr;
   const float sl = kLog2e / sqrtf((float)D);
 
   // key range of the workgroup and of this wave
   const int last_pos = min(N, p0 + PB);          // exclusive
-  const int kend = a.causal ? min(M, last_pos) : M;
+  const int kend = causal ? min(M, last_pos) : M;
   const int ntiles = (kend + C::BN - 1) / C::BN;
   const int w_last = min(N, wp0 + C::RW);        // exclusive
-  const int w_kend = (wp0 >= N) ? 0 : (a.causal ? min(M, w_last) : M);
+  const int w_kend = (wp0 >= N) ? 0 : (causal ? min(M, w_last) : M);
 
-  // Q operands for this wave's rows
+  // Q operands for this wave's rows (zero for rows past N and padded d)
   u32x4 qop[C::QB][C::QCH];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
@@ -132,8 +142,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
 #pragma unroll
     for (int u = 0; u < C::QCH; ++u) {
       const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qop[qb][u] = (pv && d0 < D) ? ld16(qp + (size_t)d0 * C::ELT) : z;
+      const bool dv = DIRECT || d0 < D;
+      qop[qb][u] = sel16(pv && dv, ld16(qp + (size_t)(dv ? d0 : 0) * C::ELT));
     }
   }
 
@@ -155,18 +165,36 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       const int i = idx / C::BN;
       const int key = k0 + (idx - i * C::BN);
       const int pos = p0 + i;
-      if (pos < N && key < kend && (!a.causal || key <= pos) && mb[(size_t)pos * M + key]) any = 1;
+      if (pos < N && key < kend && (!causal || key <= pos) && mb[(size_t)pos * M + key]) any = 1;
     }
     return __syncthreads_or(any) != 0;
   };
   auto next_tile = [&](int t) -> int {
-    if (mb == nullptr) return t;
-    while (t < ntiles && !tile_visible(t)) ++t;
+    if constexpr (MASKED) {
+      while (t < ntiles && !tile_visible(t)) ++t;
+    }
     return t;
   };
 
-  u32x4 stage[C::PPT];
-  auto load_stage = [&](int t) {
+  // ---- tile copies -----------------------------------------------------------
+  u32x4 stage[DIRECT ? 1 : C::PPT];
+  auto dma_tile = [&](int t, int buf) {   // DIRECT: global -> LDS, no registers
+    const int k0 = t * C::BN;
+    lds_char* sb = smem + buf * C::STAGE;
+    const int lrow = lane / C::CPR;            // row within the instruction's 1 KB
+    const int slot = lane - lrow * C::CPR;     // LDS chunk slot of this lane
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_TILE; ++i) {
+      const int row = (i * kWaves + w) * C::RPI + lrow;
+      const int key = min(k0 + row, M - 1);
+      const int kc = slot ^ (row & C::KSWZ);          // K chunk stored at `slot`
+      const int vc = slot ^ (2 * (row & C::VSWZ));    // V chunk stored at `slot`
+      lds_char* dst = sb + (i * kWaves + w) * 1024;
+      dma16(kp + ((size_t)key * DP + kc * 8) * 2, dst);
+      dma16(vp + ((size_t)key * DP + vc * 8) * 2, dst + C::TILE);
+    }
+  };
+  auto load_stage = [&](int t) {          // staged: global -> registers
     const int k0 = t * C::BN;
 #pragma unroll
     for (int it = 0; it < C::PPT; ++it) {
@@ -178,11 +206,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       const int key = k0 + row;
       const int d0 = chunk * (16 / C::ELT);
       const char* src = which ? vp : kp;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      stage[it] = (key < M && d0 < D) ? ld16(src + ((size_t)key * D + d0) * C::ELT) : z;
+      const bool ok = key < M && d0 < D;
+      stage[it] = sel16(ok, ld16(src + ((size_t)min(key, M - 1) * D + (ok ? d0 : 0)) * C::ELT));
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf) {       // staged: registers -> LDS
     lds_char* sb = smem + buf * C::STAGE;
 #pragma unroll
     for (int it = 0; it < C::PPT; ++it) {
@@ -198,14 +226,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
 
   int t = next_tile(0);
   if (t < ntiles) {
-    load_stage(t);
-    store_stage(0);
+    if constexpr (DIRECT) {
+      dma_tile(t, 0);
+    } else {
+      load_stage(t);
+      store_stage(0);
+    }
   }
   __syncthreads();
   int cur = 0;
   while (t < ntiles) {
     const int tn = next_tile(t + 1);
-    if (tn < ntiles) load_stage(tn);
+    if (tn < ntiles) {
+      if constexpr (DIRECT) dma_tile(tn, cur ^ 1);
+      else load_stage(tn);
+    }
 
     const int k0 = t * C::BN;
     if (k0 < w_kend) {
@@ -235,22 +270,24 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
           }
         }
       }
-      // ---- visibility ---------------------------------------------------
-      const bool need_mask = (mb != nullptr) || (k0 + C::BN > M) ||
-                             (a.causal && k0 + C::BN - 1 > wp0);
+      // ---- visibility (only tiles that need it) -------------------------
+      const bool need_mask = MASKED || (k0 + C::BN > M) || (causal && k0 + C::BN - 1 > wp0);
       if (need_mask) {
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
           const int pos = wp0 + 16 * qb + c16;
-          const bool pv = pos < N;
+          const int lim = causal ? min(pos + 1, M) : M;  // keys < lim are in range
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int key = k0 + 16 * kb + 4 * qg + r;
-              bool vis = pv && key < M && (!a.causal || key <= pos);
-              if (mb) vis = vis && (mb[(size_t)(pv ? pos : 0) * M + (key < M ? key : 0)] != 0);
-              if (!vis) sc[qb][kb][r] = kNegInf;
+              bool vis = key < lim;
+              if constexpr (MASKED) {
+                const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * M + min(key, M - 1)];
+                vis = vis && (mbyte != 0) && (pos < N);
+              }
+              sc[qb][kb][r] = vis ? sc[qb][kb][r] : kNegInf;
             }
           }
         }
@@ -286,10 +323,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
         if constexpr (BF16) {
 #pragma unroll
           for (int c = 0; c < C::NKB / 2; ++c) {
-            float pp[8] = {pf[qb][2 * c][0], pf[qb][2 * c][1], pf[qb][2 * c][2], pf[qb][2 * c][3],
-                           pf[qb][2 * c + 1][0], pf[qb][2 * c + 1][1], pf[qb][2 * c + 1][2],
-                           pf[qb][2 * c + 1][3]};
-            bop[qb][c] = to_bf16x8(pp);
+            u32x4 wv;
+            wv[0] = pack_bf16x2(pf[qb][2 * c][0], pf[qb][2 * c][1]);
+            wv[1] = pack_bf16x2(pf[qb][2 * c][2], pf[qb][2 * c][3]);
+            wv[2] = pack_bf16x2(pf[qb][2 * c + 1][0], pf[qb][2 * c + 1][1]);
+            wv[3] = pack_bf16x2(pf[qb][2 * c + 1][2], pf[qb][2 * c + 1][3]);
+            bop[qb][c] = __builtin_bit_cast(bf16x8, wv);
           }
         }
       }
@@ -326,7 +365,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       }
     }
 
-    if (tn < ntiles) store_stage(cur ^ 1);
+    if constexpr (!DIRECT) {
+      if (tn < ntiles) store_stage(cur ^ 1);
+    }
     __syncthreads();
     cur ^= 1;
     t = tn;
@@ -359,17 +400,29 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   }
 }
 
-template <bool BF16, int DP, bool OUTF32>
-hipError_t launch_dp(const PrefillArgs& a, hipStream_t stream) {
+template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
+hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   using C = PreCfg<BF16, DP>;
   const int HG = (a.g % 4 == 0) ? 4 : ((a.g % 2 == 0) ? 2 : 1);
   const int PB = (kWaves / HG) * C::RW;
   const int npb = (a.N + PB - 1) / PB;
   const int units = a.B * a.H_kv * (a.g / HG);
   const long blocks = (long)npb * units;
-  hipLaunchKernelGGL((prefill_kernel<BF16, DP, OUTF32>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, a, HG, units, npb);
+  hipLaunchKernelGGL((prefill_kernel<BF16, DP, DIRECT, MASKED, OUTF32>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, stream, a, HG, units, npb);
   return hipGetLastError();
+}
+
+template <bool BF16, int DP, bool OUTF32>
+hipError_t launch_dp(const PrefillArgs& a, hipStream_t stream) {
+  if constexpr (BF16) {
+    if (a.D == DP) {
+      return a.mask ? launch_k<BF16, DP, true, true, OUTF32>(a, stream)
+                    : launch_k<BF16, DP, true, false, OUTF32>(a, stream);
+    }
+  }
+  return a.mask ? launch_k<BF16, DP, false, true, OUTF32>(a, stream)
+                : launch_k<BF16, DP, false, false, OUTF32>(a, stream);
 }
 
 template <bool BF16, bool OUTF32>
