@@ -45,7 +45,9 @@ KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
     "prefill": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "prefill.hip"),
 }
-KERNEL_NAMES = {"decode": "decode_kernel", "prefill": "prefill_kernel"}
+# the kernels one call launches (decode: main kernel, then the split merge)
+KERNEL_NAMES = {"decode": "decode_kernel+decode_merge_kernel", "prefill": "prefill_kernel"}
+KERNEL_PATTERNS = {"decode": ("decode_kernel", "decode_merge_kernel"), "prefill": ("prefill_kernel",)}
 
 
 def log(*a):
@@ -86,54 +88,90 @@ def setup(name, torch, copies=1):
 
 
 def make_call(info, torch):
+    """One prepared op per input copy; call(i) enqueues step i."""
     import grouped_query_attention_fwd_amd as gqa
     w = info["w"]
-    outs = []
+    ops = []
     if w.kind == "decode":
-        ws = torch.zeros(max(1, gqa.decode_workspace_size(w.B, w.H, w.H_kv, w.M, w.D)),
+        ws = torch.empty(max(1, gqa.decode_workspace_size(w.B, w.H, w.H_kv, w.M, w.D)),
                          dtype=torch.uint8, device="cuda")
         for (q, k, v, m) in info["sets"]:
-            outs.append(torch.empty_like(q))
-
-        def call(i):
-            q, k, v, m = info["sets"][i % len(info["sets"])]
-            gqa.decode(q, k, v, m, out=outs[i % len(outs)], workspace=ws)
+            ops.append(gqa.decode_op(q, k, v, m, workspace=ws))
     else:
         for (q, k, v, m) in info["sets"]:
-            outs.append(torch.empty_like(q))
+            ops.append(gqa.prefill_op(q, k, v, m, causal=info["cpu"][4]))
 
-        def call(i):
-            q, k, v, m = info["sets"][i % len(info["sets"])]
-            gqa.prefill(q, k, v, m, causal=info["cpu"][4], out=outs[i % len(outs)])
+    def call(i):
+        ops[i % len(ops)]()
     return call
 
 
 def time_workload(info, steps, warmup, torch):
+    """Eager timing on the launch stream: HIP events around K back-to-back
+    steps (throughput), then around every step of a second pass (per-launch
+    duration)."""
     call = make_call(info, torch)
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # whole job: K back-to-back steps between two events
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record()
     for i in range(steps):
-        starts[i].record()
         call(warmup + i)
-        ends[i].record()
     t_all1.record()
     torch.cuda.synchronize()
-    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     total_ms = t_all0.elapsed_time(t_all1)
-    return {
+    # per launch: an event pair around every call of a second timed pass
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        starts[i].record()
+        call(warmup + steps + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+    res = {
         "ms_per_step": total_ms / steps,
         "launch_ms_avg": sum(per) / len(per),
-        "launch_ms_p10": per[max(0, int(0.1 * len(per)) - 0)],
+        "launch_ms_p10": per[int(0.1 * (len(per) - 1))],
         "launch_ms_p50": per[len(per) // 2],
-        "launch_ms_p90": per[min(len(per) - 1, int(0.9 * len(per)))],
+        "launch_ms_p90": per[int(0.9 * (len(per) - 1))],
     }
+    # cross-check without host launch overhead: the same calls replayed
+    # from a captured HIP graph
+    try:
+        reps = min(steps, 20)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            call(0)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(reps):
+                    call(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(3):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            best = t if best is None else min(best, t)
+        res["graph_ms_per_launch"] = best
+    except Exception as exc:   # noqa: BLE001 - report, keep the eager numbers
+        log(f"[bench] graph replay unavailable: {exc}")
+        res["graph_ms_per_launch"] = None
+    return res
 
 
 def traffic_for(kind, workload, launch_units):
@@ -170,11 +208,14 @@ def result_for(info, timing):
         unit = "TFLOP/s"
     roof["traffic"] = traffic_for(kind, w.name, info["units"])
     roof["kernel"] = KERNEL_NAMES[kind]
+    roof["duration_us"] = round(timing["launch_ms_avg"] * 1e3, 2)
     return {
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
         "ms_per_step": round(timing["ms_per_step"], 5),
         "launch_us": {k[len("launch_ms_"):]: round(v * 1e3, 2) for k, v in timing.items()
                       if k.startswith("launch_ms_")},
+        "graph_us_per_launch": (None if timing.get("graph_ms_per_launch") is None
+                                else round(timing["graph_ms_per_launch"] * 1e3, 2)),
         "algorithmic_units_per_launch": info["units"],
         "roofline": roof,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "M": w.M,
@@ -183,9 +224,10 @@ def result_for(info, timing):
 
 
 # ------------------------------------------------------------- cpu baseline
-def cpu_baseline(info, budget_s=15.0):
-    """Time the fp64 oracle on a bounded sample of the same workload (whole
-    batch rows, first rows first) and scale to the metric's unit."""
+def cpu_baseline(info, budget_s=12.0, max_rows=None):
+    """Time the fp64 oracle on a bounded sample of the same workload: whole
+    batch rows in order (wrapping round, so a small workload is repeated)
+    until about budget_s seconds of CPU work, scaled to the metric's unit."""
     import numpy as np
 
     import oracle
@@ -197,7 +239,8 @@ def cpu_baseline(info, budget_s=15.0):
     q, k, v, mask, causal = info["cpu"]
     w = info["w"]
     done_units, t_used, rows = 0, 0.0, 0
-    for b in range(w.B):
+    while t_used < budget_s and (max_rows is None or rows < max_rows):
+        b = rows % w.B
         qb = q[b:b + 1].float().numpy().astype(np.float64)
         kb = k[b:b + 1].float().numpy().astype(np.float64)
         vb = v[b:b + 1].float().numpy().astype(np.float64)
@@ -207,14 +250,13 @@ def cpu_baseline(info, budget_s=15.0):
         t_used += time.perf_counter() - t0
         rows += 1
         done_units += info["units"] / w.B
-        if t_used >= budget_s:
-            break
     if w.kind == "decode":
         val, unit = done_units / t_used / 1e9, "GB/s"
     else:
         val, unit = done_units / t_used / 1e12, "TFLOP/s"
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {w.B} batch rows of {w.name} ({t_used:.1f} s of fp64 numpy)"}
+            "sample": f"{rows} batch rows of {w.name} ({rows / w.B:.2f} x the workload; "
+                      f"{t_used:.1f} s of fp64 numpy on the host)"}
 
 
 # ---------------------------------------------------------- counter support
@@ -232,10 +274,14 @@ def profile_run(name, steps=3):
     torch.cuda.synchronize()
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
-    """Read two rocprofv3 --pmc counter_collection.csv outputs (FETCH_SIZE and
-    WRITE_SIZE, KiB per dispatch), calibrate with the 1 GiB copy kernel and
-    store bytes per launch per workload."""
+def summarize_pmc(workload, fetch_dir, write_dir):
+    """Traffic per call from two rocprofv3 --pmc runs of --profile-run
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled
+    by what it reads for the 1 GiB copy in the same run (factor = true bytes
+    / counted bytes), then summed over the kernels of one call."""
+    import workloads
+    kind = workloads.by_name(workload).kind
+
     def load(d, counter):
         rows = []
         for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -245,18 +291,23 @@ def summarize_pmc(fetch_dir, write_dir, out_path=TRAFFIC_FILE):
                         rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
         return rows
 
-    res = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+    out = {"workload": workload, "kernel": KERNEL_NAMES[kind], "source_sha": source_sha(kind)}
+    total = 0.0
+    for counter, d, copy_bytes in (("FETCH_SIZE", fetch_dir, 1 << 30), ("WRITE_SIZE", write_dir, 1 << 30)):
         rows = load(d, counter)
-        copy = [v for n, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
-        known_kib = (1 << 30) / 1024.0
-        factor = known_kib / max(copy) if copy else 1.0
-        for kind, kname in KERNEL_NAMES.items():
-            vals = [v for n, v in rows if kname in n]
+        copy = [val for n, val in rows if "copy" in n.lower() or "elementwise" in n.lower()]
+        factor = (copy_bytes / 1024.0) / max(copy) if copy and max(copy) > 0 else None
+        per_call = 0.0
+        for pat in KERNEL_PATTERNS[kind]:
+            vals = [val for n, val in rows if (pat + "<") in n or n.endswith(pat)]
             if vals:
-                res.setdefault(kind, {})[counter] = {"kib_per_dispatch": sum(vals) / len(vals),
-                                                     "copy_factor": factor}
-    return res
+                per_call += sum(vals) / len(vals)
+        out[counter] = {"kib_per_call": round(per_call, 1),
+                        "copy_kib_counted": max(copy) if copy else None,
+                        "copy_factor": None if factor is None else round(factor, 4)}
+        total += per_call * 1024.0 * (factor if factor else 1.0)
+    out["bytes_per_launch"] = int(total)
+    return out
 
 
 def main():
@@ -268,11 +319,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None)
     ap.add_argument("--profile-run", default=None)
-    ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs=3, default=None,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
+        ent = summarize_pmc(*args.summarize_pmc)
+        try:
+            with open(TRAFFIC_FILE) as f:
+                data = json.load(f)
+        except (OSError, ValueError):
+            data = {}
+        data[ent["workload"]] = ent
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+        print(json.dumps(ent, indent=1))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this grouped-query attention forward runs on a "
@@ -330,6 +391,7 @@ def main():
         "config": p["config"],
         "roofline": p["roofline"],
         "launch_us": p["launch_us"],
+        "graph_us_per_launch": p["graph_us_per_launch"],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a CPU sample")
@@ -339,7 +401,8 @@ def main():
     sec = [results[n] for n in names if n != primary]
     if sec:
         line["secondary"] = [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step",
-                                                "launch_us", "roofline")} for r in sec]
+                                                "launch_us", "graph_us_per_launch", "roofline")}
+                             for r in sec]
     print(json.dumps(line), flush=True)
     return 0
 

@@ -23,8 +23,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["decode", "prefill", "decode_workspace_size", "status_string",
-           "library_path", "GQAError", "load_library"]
+__all__ = ["decode", "prefill", "decode_op", "prefill_op", "decode_workspace_size",
+           "status_string", "library_path", "GQAError", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
@@ -142,10 +142,7 @@ def _out(q, out, out_dtype, shape):
     return out
 
 
-def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
-    """One decode step; see the module docstring.  workspace: optional
-    uint8 device tensor of at least decode_workspace_size(...) bytes (no
-    initialisation needed); allocated per call when omitted."""
+def _prepare_decode(q, k, v, mask, out, out_dtype, workspace):
     torch = _torch()
     _check_tensors(q, k, v, mask)
     B, H, N, D = q.shape
@@ -161,18 +158,12 @@ def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
-        code = lib.gqa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask),
-                              out.data_ptr(), B, H, H_kv, M, D, _dtype_code(q.dtype),
-                              _dtype_code(out.dtype), ws_ptr, ws_bytes, stream)
-    _check(code)
-    return out
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask), out.data_ptr(),
+            B, H, H_kv, M, D, _dtype_code(q.dtype), _dtype_code(out.dtype), ws_ptr, ws_bytes)
+    return lib, args, out, workspace
 
 
-def prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
-    """Prefill forward; see the module docstring."""
-    torch = _torch()
+def _prepare_prefill(q, k, v, mask, causal, out, out_dtype):
     _check_tensors(q, k, v, mask)
     B, H, N, D = q.shape
     _, H_kv, M, _ = k.shape
@@ -180,10 +171,56 @@ def prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
         raise ValueError("prefill mask must be [B,N,M]")
     out = _out(q, out, out_dtype, (B, H, N, D))
     lib = load_library()
-    stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask), 1 if causal else 0,
+            out.data_ptr(), B, H, H_kv, N, M, D, _dtype_code(q.dtype), _dtype_code(out.dtype))
+    return lib, args, out
+
+
+class _PreparedOp:
+    """A validated, marshalled call: calling it only passes the current
+    stream and enqueues the kernels.  The tensors it was built from must stay
+    alive and unchanged in shape while it is used."""
+
+    def __init__(self, fn, args, out, keep):
+        self._fn, self._args, self.out, self._keep = fn, args, out, keep
+        torch = _torch()
+        self._device = out.device
+        self._stream_of = torch.cuda.current_stream
+
+    def __call__(self, stream=None):
+        s = stream if stream is not None else self._stream_of(self._device)
+        _check(self._fn(*self._args, s.cuda_stream))
+        return self.out
+
+
+def decode_op(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
+    """Prepared decode call for tight loops (e.g. a serving step or HIP
+    graph capture): validation and marshalling happen once here."""
+    lib, args, out, ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace)
+    return _PreparedOp(lib.gqa_decode, args, out, (q, k, v, mask, ws))
+
+
+def prefill_op(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
+    """Prepared prefill call; see decode_op."""
+    lib, args, out = _prepare_prefill(q, k, v, mask, causal, out, out_dtype)
+    return _PreparedOp(lib.gqa_prefill, args, out, (q, k, v, mask))
+
+
+def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
+    """One decode step; see the module docstring.  workspace: optional
+    uint8 device tensor of at least decode_workspace_size(...) bytes (no
+    initialisation needed); allocated per call when omitted."""
+    torch = _torch()
+    lib, args, out, _ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace)
     with torch.cuda.device(q.device):
-        code = lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask),
-                               1 if causal else 0, out.data_ptr(), B, H, H_kv, N, M, D,
-                               _dtype_code(q.dtype), _dtype_code(out.dtype), stream)
-    _check(code)
+        _check(lib.gqa_decode(*args, torch.cuda.current_stream(q.device).cuda_stream))
+    return out
+
+
+def prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
+    """Prefill forward; see the module docstring."""
+    torch = _torch()
+    lib, args, out = _prepare_prefill(q, k, v, mask, causal, out, out_dtype)
+    with torch.cuda.device(q.device):
+        _check(lib.gqa_prefill(*args, torch.cuda.current_stream(q.device).cuda_stream))
     return out

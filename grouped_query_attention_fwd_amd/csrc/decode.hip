@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63;
   const int c16 = lane & 15;
   const int qg = lane >> 4;
@@ -239,8 +239,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
         mloc = fmaxf(mloc, x);
       }
     }
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+    mloc = rows_max(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float msl = m_use * sl;
@@ -309,8 +308,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   }
 
   // ---- merge the waves through LDS -----------------------------------
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  const float l_tot = rows_sum(l_run);
   __syncthreads();  // all waves are done with their V areas
   float* cacc = reinterpret_cast<float*>(smem_raw);              // [4][16][DP]
   float* cm = cacc + kWaves * 16 * DP;                           // [4][16]

@@ -122,4 +122,22 @@ __device__ __forceinline__ bf16x8 concat_bf16(i16x4 a, i16x4 b) {
 // Cross-lane reductions inside a wave.
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Reduce over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48),
+// every lane receiving the result.  v_permlane16_swap / v_permlane32_swap
+// exchange rows between two registers; called with the same value twice,
+// the two results hold the two halves of each pair, so combining them gives
+// the pairwise reduction whichever half lands where.  VALU only, no LDS.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace gqa

@@ -42,15 +42,26 @@
 namespace gqa {
 namespace {
 
-constexpr int kWaves = 4;
+// Waves per workgroup (4 or 8).  With 8 waves the bf16 tiles hold 128 keys,
+// so each barrier and each tile copy is amortised over twice the math.
+#ifndef GQA_PREFILL_WAVES
+#define GQA_PREFILL_WAVES 4
+#endif
+constexpr int kWaves = GQA_PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
+// Rescale threshold of the online softmax, in log2 units (weights <= 2^8).
+constexpr float kLazy = 8.f;
 
 template <bool BF16, int DP>
 struct PreCfg {
   static constexpr int ELT = BF16 ? 2 : 4;
-  static constexpr int QB = (BF16 && DP <= 128) ? 2 : 1;   // 16-row query blocks per wave
+#ifndef GQA_PREFILL_QB
+#define GQA_PREFILL_QB 2
+#endif
+  static constexpr int QB = (BF16 && DP <= 128) ? GQA_PREFILL_QB : 1;  // 16-row query blocks per wave
   static constexpr int RW = 16 * QB;                       // query rows per wave
-  static constexpr int BN = BF16 ? 64 : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
+  static constexpr int BN = BF16 ? ((kWaves == 8 && DP <= 128 && QB == 2) ? 128 : 64)
+                                 : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
   static constexpr int NKB = BN / 16;
   static constexpr int NDB = DP / 16;
   static constexpr int QCH = BF16 ? DP / 32 : DP / 16;     // 16-byte operand chunks per lane
@@ -66,9 +77,10 @@ struct PreCfg {
   static constexpr int VSWZ = (SPR < 8 ? SPR : 8) - 1;     // V row swizzle mask
   // direct copies: one wave instruction fills 1 KB = RPI rows of a tile
   static constexpr int RPI = BF16 ? 1024 / ROWB : 1;
-  static constexpr int DMA_PER_TILE = BF16 ? BN / RPI / kWaves : 0;  // per wave, per K or V tile
+  static constexpr int DMA_INSTS = BF16 ? BN / RPI : 0;                  // per K or V tile
+  static constexpr int DMA_PER_TILE = (DMA_INSTS + kWaves - 1) / kWaves;  // per wave
   static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
-  static_assert(!BF16 || (BN % (RPI * kWaves) == 0), "direct copy must split evenly");
+  static_assert(!BF16 || (BN % RPI == 0), "direct copy must cover whole rows");
 };
 
 template <bool BF16, int DP>
@@ -88,14 +100,14 @@ __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
 // DIRECT: bf16 with D == DP, tiles copied straight into LDS.
 // MASKED: a [B,N,M] mask is given.
 template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int HG, int units, int npb) {
+__global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillArgs a, int HG, int units, int npb) {
   using C = PreCfg<BF16, DP>;
   static_assert(!DIRECT || BF16, "direct copies are for bf16 tiles");
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63;
   const int c16 = lane & 15;
   const int qg = lane >> 4;
@@ -178,21 +190,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
 
   // ---- tile copies -----------------------------------------------------------
   u32x4 stage[DIRECT ? 1 : C::PPT];
-  auto dma_tile = [&](int t, int buf) {   // DIRECT: global -> LDS, no registers
+  // DIRECT copies: global -> LDS, no registers.  which = 0: K, 1: V.
+  auto dma_half = [&](int t, int buf, int which) {
     const int k0 = t * C::BN;
-    lds_char* sb = smem + buf * C::STAGE;
+    lds_char* sb = smem + buf * C::STAGE + which * C::TILE;
+    const char* src = which ? vp : kp;
     const int lrow = lane / C::CPR;            // row within the instruction's 1 KB
     const int slot = lane - lrow * C::CPR;     // LDS chunk slot of this lane
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_TILE; ++i) {
+      if (C::DMA_INSTS % kWaves != 0 && i * kWaves + w >= C::DMA_INSTS) break;  // wave-uniform
       const int row = (i * kWaves + w) * C::RPI + lrow;
       const int key = min(k0 + row, M - 1);
-      const int kc = slot ^ (row & C::KSWZ);          // K chunk stored at `slot`
-      const int vc = slot ^ (2 * (row & C::VSWZ));    // V chunk stored at `slot`
-      lds_char* dst = sb + (i * kWaves + w) * 1024;
-      dma16(kp + ((size_t)key * DP + kc * 8) * 2, dst);
-      dma16(vp + ((size_t)key * DP + vc * 8) * 2, dst + C::TILE);
+      // the chunk that belongs at `slot` under this row's swizzle
+      const int chunk = which ? (slot ^ (2 * (row & C::VSWZ))) : (slot ^ (row & C::KSWZ));
+      dma16(src + ((size_t)key * DP + chunk * 8) * 2, sb + (i * kWaves + w) * 1024);
     }
+  };
+  auto dma_tile = [&](int t, int buf) {
+    dma_half(t, buf, 0);
+    dma_half(t, buf, 1);
   };
   auto load_stage = [&](int t) {          // staged: global -> registers
     const int k0 = t * C::BN;
@@ -224,6 +241,157 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
     }
   };
 
+  // ---- per-tile building blocks ------------------------------------------
+  typedef f32x4 Scores[C::QB][C::NKB];
+
+  // S^T = K Q^T for the tile in K buffer `kbuf_lds`.
+  auto tile_scores = [&](const lds_char* kbuf_lds, Scores& sc) {
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) sc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int u = 0; u < C::QCH; ++u) {
+        const u32x4 kop = lds_ld16(kbuf_lds, k_off<BF16, DP>(16 * kb + c16, 4 * u + qg));
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          if constexpr (BF16) {
+            sc[qb][kb] = mfma_bf16(__builtin_bit_cast(bf16x8, kop),
+                                   __builtin_bit_cast(bf16x8, qop[qb][u]), sc[qb][kb]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc[qb][kb] = mfma_f32(__uint_as_float(kop[e]), __uint_as_float(qop[qb][u][e]), sc[qb][kb]);
+          }
+        }
+      }
+    }
+  };
+  // Invisible (position, key) pairs of tile t get -inf; only tiles that
+  // cross the diagonal, the end of the keys or a mask pay for this.
+  auto tile_mask = [&](int t, Scores& sc) {
+    const int k0 = t * C::BN;
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int pos = wp0 + 16 * qb + c16;
+      const int lim = causal ? min(pos + 1, M) : M;  // keys < lim are in range
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kb + 4 * qg + r;
+          bool vis = key < lim;
+          if constexpr (MASKED) {
+            const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * M + min(key, M - 1)];
+            vis = vis && (mbyte != 0) && (pos < N);
+          }
+          sc[qb][kb][r] = vis ? sc[qb][kb][r] : kNegInf;
+        }
+      }
+    }
+  };
+  // Online softmax and O^T += V^T P^T for one tile.
+  // Weights are p = 2^(s*sl - m_ref*sl) against a per-row reference max
+  // m_ref (m_run).  The reference, and with it acc and l, only moves when
+  // some row of the wave has a score more than kLazy (log2 units) above it,
+  // so p <= 2^kLazy and most tiles skip the rescale; softmax does not depend
+  // on the reference, so the result is the same.
+  // The weights are formed one 32-key half at a time and each half's P.V
+  // MFMAs follow it, so the exp work of the second half can overlap the
+  // matrix-core work of the first.
+  auto tile_softmax_pv = [&](Scores& sc, lds_char* vbuf_lds) {
+    float mloc[C::QB];
+    bool bump = false;
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+      mx = rows_max(mx);
+      mloc[qb] = mx;
+      bump = bump || ((mx - m_run[qb]) * sl > kLazy);
+    }
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {   // wave-uniform, rare
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mloc[qb]);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m_run[qb] - m_new) * sl);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < C::NDB; ++i) acc[qb][i] *= alpha;
+      }
+    }
+    float msl[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) msl[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb] * sl;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int c = 0; c < C::NKB / 2; ++c) {
+        bf16x8 bop[C::QB];
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          float pp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pp[e] = exp2_hw(fmaf(sc[qb][2 * c + (e >> 2)][e & 3], sl, -msl[qb]));
+            l_run[qb] += pp[e];
+          }
+          u32x4 wv;
+          wv[0] = pack_bf16x2(pp[0], pp[1]);
+          wv[1] = pack_bf16x2(pp[2], pp[3]);
+          wv[2] = pack_bf16x2(pp[4], pp[5]);
+          wv[3] = pack_bf16x2(pp[6], pp[7]);
+          bop[qb] = __builtin_bit_cast(bf16x8, wv);
+        }
+        const int row_a = 32 * c + 4 * qg + (c16 >> 2);
+        const int row_b = row_a + 16;
+        const int within = (c16 & 1) << 3;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const int chunk = 2 * db + ((c16 & 3) >> 1);
+          const i16x4 ta = lds_ld_tr16(vbuf_lds, v_off<BF16, DP>(row_a, chunk) + within);
+          const i16x4 tb = lds_ld_tr16(vbuf_lds, v_off<BF16, DP>(row_b, chunk) + within);
+          const bf16x8 vop = concat_bf16(ta, tb);
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_bf16(vop, bop[qb], acc[qb][db]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        float pf[C::QB][4];
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pf[qb][r] = exp2_hw(fmaf(sc[qb][kb][r], sl, -msl[qb]));
+            l_run[qb] += pf[qb][r];
+          }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * kb + 4 * qg + r;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const float vv = lds_ldf(vbuf_lds, row * C::ROWB + (16 * db + c16) * 4);
+#pragma unroll
+            for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_f32(vv, pf[qb][r], acc[qb][db]);
+          }
+        }
+      }
+    }
+  };
+  auto tile_needs_mask = [&](int t) {
+    const int k0 = t * C::BN;
+    return MASKED || (k0 + C::BN > M) || (causal && k0 + C::BN - 1 > wp0);
+  };
+  auto kbuf = [&](int buf) { return smem + buf * C::STAGE; };
+  auto vbuf = [&](int buf) { return smem + buf * C::STAGE + C::TILE; };
+
   int t = next_tile(0);
   if (t < ntiles) {
     if constexpr (DIRECT) {
@@ -241,130 +409,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
       if constexpr (DIRECT) dma_tile(tn, cur ^ 1);
       else load_stage(tn);
     }
-
-    const int k0 = t * C::BN;
-    if (k0 < w_kend) {
-      lds_char* kb_lds = smem + cur * C::STAGE;
-      lds_char* vb_lds = kb_lds + C::TILE;
-      // ---- S^T = K Q^T --------------------------------------------------
-      f32x4 sc[C::QB][C::NKB];
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) sc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int u = 0; u < C::QCH; ++u) {
-          const u32x4 kop = lds_ld16(kb_lds, k_off<BF16, DP>(16 * kb + c16, 4 * u + qg));
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) {
-            if constexpr (BF16) {
-              sc[qb][kb] = mfma_bf16(__builtin_bit_cast(bf16x8, kop),
-                                     __builtin_bit_cast(bf16x8, qop[qb][u]), sc[qb][kb]);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                sc[qb][kb] = mfma_f32(__uint_as_float(kop[e]), __uint_as_float(qop[qb][u][e]), sc[qb][kb]);
-            }
-          }
-        }
-      }
-      // ---- visibility (only tiles that need it) -------------------------
-      const bool need_mask = MASKED || (k0 + C::BN > M) || (causal && k0 + C::BN - 1 > wp0);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) {
-          const int pos = wp0 + 16 * qb + c16;
-          const int lim = causal ? min(pos + 1, M) : M;  // keys < lim are in range
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = k0 + 16 * kb + 4 * qg + r;
-              bool vis = key < lim;
-              if constexpr (MASKED) {
-                const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * M + min(key, M - 1)];
-                vis = vis && (mbyte != 0) && (pos < N);
-              }
-              sc[qb][kb][r] = vis ? sc[qb][kb][r] : kNegInf;
-            }
-          }
-        }
-      }
-      // ---- online softmax -----------------------------------------------
-      bf16x8 bop[C::QB][C::NKB / 2 > 0 ? C::NKB / 2 : 1];
-      float pf[C::QB][C::NKB][4];
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-        float mloc = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[qb][kb][r]);
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-        const float m_new = fmaxf(m_run[qb], mloc);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float msl = m_use * sl;
-        const float alpha = exp2_hw(m_run[qb] * sl - msl);
-        m_run[qb] = m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pf[qb][kb][r] = exp2_hw(fmaf(sc[qb][kb][r], sl, -msl));
-            psum += pf[qb][kb][r];
-          }
-        l_run[qb] = fmaf(l_run[qb], alpha, psum);
-#pragma unroll
-        for (int i = 0; i < C::NDB; ++i) acc[qb][i] *= alpha;
-        if constexpr (BF16) {
-#pragma unroll
-          for (int c = 0; c < C::NKB / 2; ++c) {
-            u32x4 wv;
-            wv[0] = pack_bf16x2(pf[qb][2 * c][0], pf[qb][2 * c][1]);
-            wv[1] = pack_bf16x2(pf[qb][2 * c][2], pf[qb][2 * c][3]);
-            wv[2] = pack_bf16x2(pf[qb][2 * c + 1][0], pf[qb][2 * c + 1][1]);
-            wv[3] = pack_bf16x2(pf[qb][2 * c + 1][2], pf[qb][2 * c + 1][3]);
-            bop[qb][c] = __builtin_bit_cast(bf16x8, wv);
-          }
-        }
-      }
-      // ---- O^T += V^T P^T -----------------------------------------------
-      if constexpr (BF16) {
-#pragma unroll
-        for (int c = 0; c < C::NKB / 2; ++c) {
-          const int row_a = 32 * c + 4 * qg + (c16 >> 2);
-          const int row_b = row_a + 16;
-          const int within = (c16 & 1) << 3;
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const int chunk = 2 * db + ((c16 & 3) >> 1);
-            const i16x4 ta = lds_ld_tr16(vb_lds, v_off<BF16, DP>(row_a, chunk) + within);
-            const i16x4 tb = lds_ld_tr16(vb_lds, v_off<BF16, DP>(row_b, chunk) + within);
-            const bf16x8 vop = concat_bf16(ta, tb);
-#pragma unroll
-            for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_bf16(vop, bop[qb][c], acc[qb][db]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * kb + 4 * qg + r;
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const float vv = lds_ldf(vb_lds, row * C::ROWB + (16 * db + c16) * 4);
-#pragma unroll
-              for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_f32(vv, pf[qb][kb][r], acc[qb][db]);
-            }
-          }
-      }
+    if (t * C::BN < w_kend) {
+      Scores sc;
+      tile_scores(kbuf(cur), sc);
+      if (tile_needs_mask(t)) tile_mask(t, sc);
+      tile_softmax_pv(sc, vbuf(cur));
     }
-
     if constexpr (!DIRECT) {
       if (tn < ntiles) store_stage(cur ^ 1);
     }
@@ -376,8 +426,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a, int
   // ---- epilogue: O = acc / l ------------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    float lt = l_run[qb] + shfl_xor_f(l_run[qb], 16);
-    lt += shfl_xor_f(lt, 32);
+    const float lt = rows_sum(l_run[qb]);
     const int pos = wp0 + 16 * qb + c16;
     if (pos >= N) continue;
     const size_t obase = (((size_t)b * a.H + h) * N + pos) * (size_t)D;
