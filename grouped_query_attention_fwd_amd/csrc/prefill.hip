@@ -49,6 +49,9 @@ namespace {
 #endif
 constexpr int kWaves = GQA_PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
+#ifndef GQA_PREFILL_XCD_MAJOR
+#define GQA_PREFILL_XCD_MAJOR 1
+#endif
 // Rescale threshold of the online softmax, in log2 units (weights <= 2^8).
 constexpr float kLazy = 8.f;
 
@@ -60,7 +63,10 @@ struct PreCfg {
 #endif
   static constexpr int QB = (BF16 && DP <= 128) ? GQA_PREFILL_QB : 1;  // 16-row query blocks per wave
   static constexpr int RW = 16 * QB;                       // query rows per wave
-  static constexpr int BN = BF16 ? ((kWaves == 8 && DP <= 128 && QB == 2) ? 128 : 64)
+#ifndef GQA_PREFILL_BN
+#define GQA_PREFILL_BN 64
+#endif
+  static constexpr int BN = BF16 ? GQA_PREFILL_BN
                                  : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
   static constexpr int NKB = BN / 16;
   static constexpr int NDB = DP / 16;
@@ -69,7 +75,6 @@ struct PreCfg {
   static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16; // LDS row stride
   static constexpr int TILE = BN * ROWB;                   // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;                   // K + V
-  static constexpr int LDS_BYTES = 2 * STAGE;              // double buffered
   static constexpr int PIECES = 2 * BN * CPR;              // 16-byte pieces per stage
   static constexpr int PPT = PIECES / kThreads;            // pieces per thread
   static constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;   // K row swizzle mask
@@ -100,11 +105,18 @@ __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
 // DIRECT: bf16 with D == DP, tiles copied straight into LDS.
 // MASKED: a [B,N,M] mask is given.
 template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
-__global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillArgs a, int HG, int units, int npb) {
+__global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillArgs a, int HG, int units, int npb,
+                                                                     int xcd_major) {
   using C = PreCfg<BF16, DP>;
   static_assert(!DIRECT || BF16, "direct copies are for bf16 tiles");
-  __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
-  lds_char* smem = (lds_char*)smem_raw;
+  // Two stages as two distinct LDS objects: with the loop unrolled by two
+  // every access names its stage statically, so the compiler can tell that
+  // reads of one stage never alias the copy in flight into the other (it
+  // would otherwise wait for that copy before each transposing V read).
+  __shared__ __attribute__((aligned(16))) char stage0_raw[C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1_raw[C::STAGE];
+  lds_char* const st0 = (lds_char*)stage0_raw;
+  lds_char* const st1 = (lds_char*)stage1_raw;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -116,9 +128,22 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   const int N = a.N, M = a.M;
   const bool causal = a.causal;
   const int groups_per_kv = a.g / HG;
+  // Workgroup -> (unit, position block).  Workgroups are dispatched to the
+  // 8 XCDs round-robin (L % 8).  With xcd_major each XCD walks its own units
+  // one after another (all blocks of a unit, heaviest first), so the K/V
+  // tiles in flight on an XCD come from about one unit and stay in its L2.
   const int L = blockIdx.x;
-  const int unit = L % units;
-  const int pbi = L / units;
+  int unit, pbi;
+  if (xcd_major) {
+    const int x = L & 7;
+    const int i = L >> 3;
+    const int lu = i / npb;
+    pbi = i - lu * npb;
+    unit = lu * 8 + x;
+  } else {
+    unit = L % units;
+    pbi = L / units;
+  }
   const int pblk = causal ? (npb - 1 - pbi) : pbi;
   const int b = unit / (a.H_kv * groups_per_kv);
   const int rem = unit - b * (a.H_kv * groups_per_kv);
@@ -191,9 +216,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // ---- tile copies -----------------------------------------------------------
   u32x4 stage[DIRECT ? 1 : C::PPT];
   // DIRECT copies: global -> LDS, no registers.  which = 0: K, 1: V.
-  auto dma_half = [&](int t, int buf, int which) {
+  auto dma_half = [&](int t, lds_char* dst_tile, int which) {
     const int k0 = t * C::BN;
-    lds_char* sb = smem + buf * C::STAGE + which * C::TILE;
     const char* src = which ? vp : kp;
     const int lrow = lane / C::CPR;            // row within the instruction's 1 KB
     const int slot = lane - lrow * C::CPR;     // LDS chunk slot of this lane
@@ -204,12 +228,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int key = min(k0 + row, M - 1);
       // the chunk that belongs at `slot` under this row's swizzle
       const int chunk = which ? (slot ^ (2 * (row & C::VSWZ))) : (slot ^ (row & C::KSWZ));
-      dma16(src + ((size_t)key * DP + chunk * 8) * 2, sb + (i * kWaves + w) * 1024);
+      dma16(src + ((size_t)key * DP + chunk * 8) * 2, dst_tile + (i * kWaves + w) * 1024);
     }
-  };
-  auto dma_tile = [&](int t, int buf) {
-    dma_half(t, buf, 0);
-    dma_half(t, buf, 1);
   };
   auto load_stage = [&](int t) {          // staged: global -> registers
     const int k0 = t * C::BN;
@@ -227,8 +247,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       stage[it] = sel16(ok, ld16(src + ((size_t)min(key, M - 1) * D + (ok ? d0 : 0)) * C::ELT));
     }
   };
-  auto store_stage = [&](int buf) {       // staged: registers -> LDS
-    lds_char* sb = smem + buf * C::STAGE;
+  auto store_stage = [&](lds_char* sb) {  // staged: registers -> LDS
 #pragma unroll
     for (int it = 0; it < C::PPT; ++it) {
       const int piece = it * kThreads + tid;
@@ -389,37 +408,49 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     const int k0 = t * C::BN;
     return MASKED || (k0 + C::BN > M) || (causal && k0 + C::BN - 1 > wp0);
   };
-  auto kbuf = [&](int buf) { return smem + buf * C::STAGE; };
-  auto vbuf = [&](int buf) { return smem + buf * C::STAGE + C::TILE; };
 
-  int t = next_tile(0);
-  if (t < ntiles) {
-    if constexpr (DIRECT) {
-      dma_tile(t, 0);
-    } else {
-      load_stage(t);
-      store_stage(0);
-    }
-  }
-  __syncthreads();
-  int cur = 0;
-  while (t < ntiles) {
-    const int tn = next_tile(t + 1);
+  // Double-buffered tile loop: the copy of the next visible tile into the
+  // other stage is issued before this tile's math (direct copies need no
+  // registers; staged copies land in registers and are written to LDS after
+  // the math).  A stage holds the K tile, then the V tile.
+  auto step = [&](int t, int tn, lds_char* rd, lds_char* wr) {
     if (tn < ntiles) {
-      if constexpr (DIRECT) dma_tile(tn, cur ^ 1);
-      else load_stage(tn);
+      if constexpr (DIRECT) {
+        dma_half(tn, wr, 0);
+        dma_half(tn, wr + C::TILE, 1);
+      } else {
+        load_stage(tn);
+      }
     }
     if (t * C::BN < w_kend) {
       Scores sc;
-      tile_scores(kbuf(cur), sc);
+      tile_scores(rd, sc);
       if (tile_needs_mask(t)) tile_mask(t, sc);
-      tile_softmax_pv(sc, vbuf(cur));
+      tile_softmax_pv(sc, rd + C::TILE);
     }
     if constexpr (!DIRECT) {
-      if (tn < ntiles) store_stage(cur ^ 1);
+      if (tn < ntiles) store_stage(wr);
     }
     __syncthreads();
-    cur ^= 1;
+  };
+  int t = next_tile(0);
+  if (t < ntiles) {
+    if constexpr (DIRECT) {
+      dma_half(t, st0, 0);
+      dma_half(t, st0 + C::TILE, 1);
+    } else {
+      load_stage(t);
+      store_stage(st0);
+    }
+  }
+  __syncthreads();
+  while (t < ntiles) {
+    int tn = next_tile(t + 1);
+    step(t, tn, st0, st1);
+    t = tn;
+    if (t >= ntiles) break;
+    tn = next_tile(t + 1);
+    step(t, tn, st1, st0);
     t = tn;
   }
 
@@ -457,8 +488,9 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   const int npb = (a.N + PB - 1) / PB;
   const int units = a.B * a.H_kv * (a.g / HG);
   const long blocks = (long)npb * units;
+  const int xcd_major = (GQA_PREFILL_XCD_MAJOR && units % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((prefill_kernel<BF16, DP, DIRECT, MASKED, OUTF32>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, stream, a, HG, units, npb);
+                     dim3(kThreads), 0, stream, a, HG, units, npb, xcd_major);
   return hipGetLastError();
 }
 
