@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 (vector and matrix), published
+WARMUP_S = 0.3                   # minimum warm-up time per workload
 METRIC = "GQA decode achieved HBM GB/s (% of peak); prefill TFLOP/s (% MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -111,9 +112,17 @@ def time_workload(info, steps, warmup, torch):
     steps (throughput), then around every step of a second pass (per-launch
     duration)."""
     call = make_call(info, torch)
-    for i in range(warmup):
-        call(i)
+    # warm-up: at least `warmup` steps and at least WARMUP_S seconds of work,
+    # so the GPU clocks have settled before the timed region
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < WARMUP_S:
+        call(done)
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup = done
     # whole job: K back-to-back steps between two events
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
@@ -135,6 +144,7 @@ def time_workload(info, steps, warmup, torch):
     torch.cuda.synchronize()
     per = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
     res = {
+        "warmup_steps_done": done,
         "ms_per_step": total_ms / steps,
         "launch_ms_avg": sum(per) / len(per),
         "launch_ms_p10": per[int(0.1 * (len(per) - 1))],
@@ -212,6 +222,7 @@ def result_for(info, timing):
     return {
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
         "ms_per_step": round(timing["ms_per_step"], 5),
+        "warmup_steps_done": timing["warmup_steps_done"],
         "launch_us": {k[len("launch_ms_"):]: round(v * 1e3, 2) for k, v in timing.items()
                       if k.startswith("launch_ms_")},
         "graph_us_per_launch": (None if timing.get("graph_ms_per_launch") is None

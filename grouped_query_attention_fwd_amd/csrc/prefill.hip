@@ -113,10 +113,14 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // every access names its stage statically, so the compiler can tell that
   // reads of one stage never alias the copy in flight into the other (it
   // would otherwise wait for that copy before each transposing V read).
-  __shared__ __attribute__((aligned(16))) char stage0_raw[C::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1_raw[C::STAGE];
-  lds_char* const st0 = (lds_char*)stage0_raw;
-  lds_char* const st1 = (lds_char*)stage1_raw;
+  __shared__ __attribute__((aligned(16))) char k0_raw[C::TILE];
+  __shared__ __attribute__((aligned(16))) char v0_raw[C::TILE];
+  __shared__ __attribute__((aligned(16))) char k1_raw[C::TILE];
+  __shared__ __attribute__((aligned(16))) char v1_raw[C::TILE];
+  lds_char* const k0s = (lds_char*)k0_raw;
+  lds_char* const v0s = (lds_char*)v0_raw;
+  lds_char* const k1s = (lds_char*)k1_raw;
+  lds_char* const v1s = (lds_char*)v1_raw;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -247,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       stage[it] = sel16(ok, ld16(src + ((size_t)min(key, M - 1) * D + (ok ? d0 : 0)) * C::ELT));
     }
   };
-  auto store_stage = [&](lds_char* sb) {  // staged: registers -> LDS
+  auto store_stage = [&](lds_char* kt, lds_char* vt) {  // staged: registers -> LDS
 #pragma unroll
     for (int it = 0; it < C::PPT; ++it) {
       const int piece = it * kThreads + tid;
@@ -255,8 +259,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int rr = piece - which * (C::BN * C::CPR);
       const int row = rr / C::CPR;
       const int chunk = rr - row * C::CPR;
-      const uint32_t off = which ? (C::TILE + v_off<BF16, DP>(row, chunk)) : k_off<BF16, DP>(row, chunk);
-      lds_st16(sb, off, stage[it]);
+      if (which) lds_st16(vt, v_off<BF16, DP>(row, chunk), stage[it]);
+      else lds_st16(kt, k_off<BF16, DP>(row, chunk), stage[it]);
     }
   };
 
@@ -413,44 +417,44 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // other stage is issued before this tile's math (direct copies need no
   // registers; staged copies land in registers and are written to LDS after
   // the math).  A stage holds the K tile, then the V tile.
-  auto step = [&](int t, int tn, lds_char* rd, lds_char* wr) {
+  auto step = [&](int t, int tn, lds_char* krd, lds_char* vrd, lds_char* kwr, lds_char* vwr) {
     if (tn < ntiles) {
       if constexpr (DIRECT) {
-        dma_half(tn, wr, 0);
-        dma_half(tn, wr + C::TILE, 1);
+        dma_half(tn, kwr, 0);
+        dma_half(tn, vwr, 1);
       } else {
         load_stage(tn);
       }
     }
     if (t * C::BN < w_kend) {
       Scores sc;
-      tile_scores(rd, sc);
+      tile_scores(krd, sc);
       if (tile_needs_mask(t)) tile_mask(t, sc);
-      tile_softmax_pv(sc, rd + C::TILE);
+      tile_softmax_pv(sc, vrd);
     }
     if constexpr (!DIRECT) {
-      if (tn < ntiles) store_stage(wr);
+      if (tn < ntiles) store_stage(kwr, vwr);
     }
     __syncthreads();
   };
   int t = next_tile(0);
   if (t < ntiles) {
     if constexpr (DIRECT) {
-      dma_half(t, st0, 0);
-      dma_half(t, st0 + C::TILE, 1);
+      dma_half(t, k0s, 0);
+      dma_half(t, v0s, 1);
     } else {
       load_stage(t);
-      store_stage(st0);
+      store_stage(k0s, v0s);
     }
   }
   __syncthreads();
   while (t < ntiles) {
     int tn = next_tile(t + 1);
-    step(t, tn, st0, st1);
+    step(t, tn, k0s, v0s, k1s, v1s);
     t = tn;
     if (t >= ntiles) break;
     tn = next_tile(t + 1);
-    step(t, tn, st1, st0);
+    step(t, tn, k1s, v1s, k0s, v0s);
     t = tn;
   }
 
