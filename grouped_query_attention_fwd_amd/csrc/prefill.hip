@@ -49,6 +49,12 @@ namespace {
 #endif
 constexpr int kWaves = GQA_PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
+#ifndef GQA_PREFILL_SETPRIO
+#define GQA_PREFILL_SETPRIO 0
+#endif
+#ifndef GQA_PREFILL_SGB
+#define GQA_PREFILL_SGB 0
+#endif
 #ifndef GQA_PREFILL_XCD_MAJOR
 #define GQA_PREFILL_XCD_MAJOR 1
 #endif
@@ -269,6 +275,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
 
   // S^T = K Q^T for the tile in K buffer `kbuf_lds`.
   auto tile_scores = [&](const lds_char* kbuf_lds, Scores& sc) {
+    if constexpr (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
@@ -291,6 +298,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
         }
       }
     }
+    if constexpr (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
   // Invisible (position, key) pairs of tile t get -inf; only tiles that
   // cross the diagonal, the end of the keys or a mask pay for this.
@@ -382,6 +390,22 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
           const bf16x8 vop = concat_bf16(ta, tb);
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_bf16(vop, bop[qb], acc[qb][db]);
+        }
+      }
+      if constexpr (GQA_PREFILL_SGB && C::NKB == 4 && C::QB == 2) {
+        // exp work of the second key half interleaved with the first half's MFMAs
+        constexpr int kMf = C::NDB * C::QB;   // MFMAs per half
+        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+#pragma unroll
+        for (int i = 0; i < kMf; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < kMf; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       }
     } else {
