@@ -4,8 +4,10 @@
 Prints ONE JSON line.  The headline is the Mistral-7B-shaped decode step
 (B16, 32 query heads, 8 KV heads, M 4096 cached keys, D 128, bf16): achieved
 HBM bandwidth = algorithmic KV bytes / time.  The same run also measures the
-Llama-2-70B-shaped decode (M 32768) and the causal bf16 prefill
-(B4, 32/8 heads, N = M = 4096, D 128; TFLOP/s over the visible pairs), which
+Llama-2-70B-shaped decode (M 32768), the causal bf16 prefill (B4, 32/8 heads,
+N = M = 4096, D 128; TFLOP/s over the visible pairs) and the paged decode of
+the Mistral-shaped batch (blocks of 16 keys scattered over a pool; mixed
+lengths, and all lengths 4096; GB/s over each sequence's own keys), which
 appear under "secondary".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
@@ -44,11 +46,15 @@ METRIC = "GQA decode achieved HBM GB/s (% of peak); prefill TFLOP/s (% MFMA peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
+    "decode_paged": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
     "prefill": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "prefill.hip"),
 }
 # the kernels one call launches (decode: main kernel, then the split merge)
-KERNEL_NAMES = {"decode": "decode_kernel+decode_merge_kernel", "prefill": "prefill_kernel"}
-KERNEL_PATTERNS = {"decode": ("decode_kernel", "decode_merge_kernel"), "prefill": ("prefill_kernel",)}
+KERNEL_NAMES = {"decode": "decode_kernel+decode_merge_kernel",
+                "decode_paged": "decode_kernel+decode_merge_kernel", "prefill": "prefill_kernel"}
+KERNEL_PATTERNS = {"decode": ("decode_kernel", "decode_merge_kernel"),
+                   "decode_paged": ("decode_kernel", "decode_merge_kernel"),
+                   "prefill": ("prefill_kernel",)}
 
 
 def log(*a):
@@ -65,9 +71,23 @@ def source_sha(kind):
 
 
 # ----------------------------------------------------------------- workloads
+def setup_paged(name, torch, copies=1):
+    import workloads
+    from grouped_query_attention_fwd_amd import accounting
+    w = workloads.paged_by_name(name)
+    cpu = workloads.make_paged_inputs(w)
+    sets = [[t.cuda() if c == 0 else t.cuda().clone() for t in cpu] for c in range(copies)]
+    elt = 2 if w.dtype == "bf16" else 4
+    info = {"w": w, "kind": "decode_paged", "cpu": cpu, "sets": sets,
+            "units": accounting.paged_decode_bytes(cpu[4].tolist(), w.H_kv, w.D, elt)}
+    return info
+
+
 def setup(name, torch, copies=1):
     import workloads
     from grouped_query_attention_fwd_amd import accounting
+    if name.startswith("decode_paged"):
+        return setup_paged(name, torch, copies)
     w = workloads.by_name(name)
     q, k, v, mask, causal = workloads.make_inputs(w)
     sets = []
@@ -77,7 +97,7 @@ def setup(name, torch, copies=1):
         else:   # distinct buffers with the same contents
             sets.append([t.cuda().clone() if t is not None else None for t in (q, k, v, mask)])
     elt = 2 if w.dtype == "bf16" else 4
-    info = {"w": w, "cpu": (q, k, v, mask, causal), "sets": sets}
+    info = {"w": w, "kind": w.kind, "cpu": (q, k, v, mask, causal), "sets": sets}
     if w.kind == "decode":
         info["units"] = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, elt)
     else:
@@ -93,7 +113,14 @@ def make_call(info, torch):
     import grouped_query_attention_fwd_amd as gqa
     w = info["w"]
     ops = []
-    if w.kind == "decode":
+    if info["kind"] == "decode_paged":
+        mb = info["sets"][0][3].shape[1]
+        ws = torch.empty(max(1, gqa.decode_paged_workspace_size(w.B, w.H, w.H_kv, mb,
+                                                                w.block_size, w.D)),
+                         dtype=torch.uint8, device="cuda")
+        for (q, kp, vp, bt, kl) in info["sets"]:
+            ops.append(gqa.decode_paged_op(q, kp, vp, bt, kl, workspace=ws))
+    elif w.kind == "decode":
         ws = torch.empty(max(1, gqa.decode_workspace_size(w.B, w.H, w.H_kv, w.M, w.D)),
                          dtype=torch.uint8, device="cuda")
         for (q, k, v, m) in info["sets"]:
@@ -200,10 +227,10 @@ def traffic_for(kind, workload, launch_units):
 
 def result_for(info, timing):
     w = info["w"]
-    kind = w.kind
+    kind = info["kind"]
     avg_s = timing["launch_ms_avg"] * 1e-3
     whole_s = timing["ms_per_step"] * 1e-3
-    if kind == "decode":
+    if kind in ("decode", "decode_paged"):
         achieved = info["units"] / avg_s / 1e9
         value = info["units"] / whole_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -218,6 +245,14 @@ def result_for(info, timing):
         unit = "TFLOP/s"
     roof["traffic"] = traffic_for(kind, w.name, info["units"])
     roof["kernel"] = KERNEL_NAMES[kind]
+    if kind == "decode_paged":
+        config = {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv,
+                  "max_len": w.max_len, "block_size": w.block_size, "D": w.D,
+                  "dtype": w.dtype, "lengths": w.lengths,
+                  "kv_len_sum": int(sum(info["cpu"][4].tolist()))}
+    else:
+        config = {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "M": w.M,
+                  "D": w.D, "dtype": w.dtype, "causal": w.causal, "padded_mask": w.padded}
     roof["duration_us"] = round(timing["launch_ms_avg"] * 1e3, 2)
     return {
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
@@ -229,8 +264,7 @@ def result_for(info, timing):
                                 else round(timing["graph_ms_per_launch"] * 1e3, 2)),
         "algorithmic_units_per_launch": info["units"],
         "roofline": roof,
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "M": w.M,
-                   "D": w.D, "dtype": w.dtype, "causal": w.causal, "padded_mask": w.padded},
+        "config": config,
     }
 
 
@@ -291,7 +325,8 @@ def summarize_pmc(workload, fetch_dir, write_dir):
     by what it reads for the 1 GiB copy in the same run (factor = true bytes
     / counted bytes), then summed over the kernels of one call."""
     import workloads
-    kind = workloads.by_name(workload).kind
+    kind = ("decode_paged" if workload.startswith("decode_paged")
+            else workloads.by_name(workload).kind)
 
     def load(d, counter):
         rows = []
@@ -365,8 +400,10 @@ def main():
     primary = args.only or "decode_mistral7b_m4096"
     names = [primary]
     if not args.skip_secondary and not args.only:
-        names += ["decode_llama70b_m32768", "prefill_causal_n4096"]
-    copies = {"decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1}
+        names += ["decode_llama70b_m32768", "prefill_causal_n4096",
+                  "decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full"]
+    copies = {"decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1,
+              "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}
     primary_info = None
     for name in names:

@@ -10,7 +10,12 @@ are not on a GPU the call raises.
         q [B,H,1,D], k/v [B,H_kv,M,D], mask [B,1,M] bool/uint8 or None
     prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None)
         q [B,H,N,D], k/v [B,H_kv,M,D], mask [B,N,M] bool/uint8 or None
+    decode_paged(q, k_pool, v_pool, block_table, kv_len, out=None, out_dtype=None,
+                 workspace=None)
+        q [B,H,1,D], pools [num_blocks,H_kv,block_size,D], block_table
+        [B,max_blocks] int32, kv_len [B] int32
     decode_workspace_size(B, H, H_kv, M, D) -> bytes
+    decode_paged_workspace_size(B, H, H_kv, max_blocks, block_size, D) -> bytes
     status_string(code) -> str
 
 Query head h reads KV head h // (H // H_kv) (repeat-interleave grouping),
@@ -23,8 +28,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["decode", "prefill", "decode_op", "prefill_op", "decode_workspace_size",
-           "status_string", "library_path", "GQAError", "load_library"]
+__all__ = ["decode", "decode_paged", "prefill", "decode_op", "decode_paged_op", "prefill_op",
+           "decode_workspace_size", "decode_paged_workspace_size", "status_string",
+           "library_path", "GQAError", "load_library"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
@@ -61,6 +67,11 @@ def load_library():
     lib.gqa_prefill.restype = i
     lib.gqa_decode_workspace_size.argtypes = [i, i, i, i, i]
     lib.gqa_decode_workspace_size.restype = sz
+    lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz,
+                                     vp]
+    lib.gqa_decode_paged.restype = i
+    lib.gqa_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.gqa_decode_paged_workspace_size.restype = sz
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -83,6 +94,11 @@ def decode_workspace_size(B, H, H_kv, M, D) -> int:
     return int(load_library().gqa_decode_workspace_size(B, H, H_kv, M, D))
 
 
+def decode_paged_workspace_size(B, H, H_kv, max_blocks, block_size, D) -> int:
+    return int(load_library().gqa_decode_paged_workspace_size(B, H, H_kv, max_blocks,
+                                                              block_size, D))
+
+
 def _torch():
     import torch
     return torch
@@ -97,7 +113,7 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
 
 
-def _check_tensors(q, k, v, mask):
+def _check_tensors(q, k, v, mask, same_batch=True):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
@@ -112,8 +128,8 @@ def _check_tensors(q, k, v, mask):
         raise ValueError("q, k, v must be on the same device")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype")
-    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
-        raise ValueError("k and v must be [B,H_kv,M,D] with q's B and D")
+    if k.shape != v.shape or k.shape[3] != q.shape[3] or (same_batch and k.shape[0] != q.shape[0]):
+        raise ValueError("k and v must have the same shape, with q's D (and B, unpaged)")
     if mask is not None:
         if not mask.is_cuda or mask.device != q.device:
             raise ValueError("mask must be on the same GPU as q")
@@ -163,6 +179,36 @@ def _prepare_decode(q, k, v, mask, out, out_dtype, workspace):
     return lib, args, out, workspace
 
 
+def _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out, out_dtype, workspace):
+    torch = _torch()
+    _check_tensors(q, k_pool, v_pool, None, same_batch=False)
+    B, H, N, D = q.shape
+    num_blocks, H_kv, block_size, _ = k_pool.shape
+    if N != 1:
+        raise ValueError("decode takes one query position (q [B,H,1,D])")
+    for name, t in (("block_table", block_table), ("kv_len", kv_len)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a tensor on the same GPU as q")
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    if tuple(kv_len.shape) != (B,):
+        raise ValueError("kv_len must be [B]")
+    max_blocks = block_table.shape[1]
+    out = _out(q, out, out_dtype, (B, H, 1, D))
+    lib = load_library()
+    need = int(lib.gqa_decode_paged_workspace_size(B, H, H_kv, max_blocks, block_size, D))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+            kv_len.data_ptr(), out.data_ptr(), B, H, H_kv, max_blocks, block_size, num_blocks,
+            D, _dtype_code(q.dtype), _dtype_code(out.dtype), ws_ptr, ws_bytes)
+    return lib, args, out, workspace
+
+
 def _prepare_prefill(q, k, v, mask, causal, out, out_dtype):
     _check_tensors(q, k, v, mask)
     B, H, N, D = q.shape
@@ -200,6 +246,16 @@ def decode_op(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
     return _PreparedOp(lib.gqa_decode, args, out, (q, k, v, mask, ws))
 
 
+def decode_paged_op(q, k_pool, v_pool, block_table, kv_len, out=None, out_dtype=None,
+                    workspace=None):
+    """Prepared paged decode call; see decode_op.  The table and lengths are
+    read by the kernel at every call, so they may change between calls."""
+    lib, args, out, ws = _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out,
+                                               out_dtype, workspace)
+    return _PreparedOp(lib.gqa_decode_paged, args, out,
+                       (q, k_pool, v_pool, block_table, kv_len, ws))
+
+
 def prefill_op(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
     """Prepared prefill call; see decode_op."""
     lib, args, out = _prepare_prefill(q, k, v, mask, causal, out, out_dtype)
@@ -214,6 +270,19 @@ def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
     lib, args, out, _ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace)
     with torch.cuda.device(q.device):
         _check(lib.gqa_decode(*args, torch.cuda.current_stream(q.device).cuda_stream))
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, block_table, kv_len, out=None, out_dtype=None,
+                 workspace=None):
+    """One decode step over a paged KV cache: key t of sequence b is row
+    t % block_size of pool block block_table[b, t // block_size], and only
+    keys t < kv_len[b] exist.  Workspace as for decode()."""
+    torch = _torch()
+    lib, args, out, _ws = _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out,
+                                                out_dtype, workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.gqa_decode_paged(*args, torch.cuda.current_stream(q.device).cuda_stream))
     return out
 
 

@@ -8,7 +8,7 @@ kv_cache_bytes is the KV-cache equation of the *Theory* section of
 
 from __future__ import annotations
 
-__all__ = ["kv_cache_bytes", "decode_bytes", "visible_pairs",
+__all__ = ["kv_cache_bytes", "decode_bytes", "paged_decode_bytes", "visible_pairs",
            "prefill_flops", "DTYPE_BYTES"]
 
 DTYPE_BYTES = {"fp32": 4, "bf16": 2}
@@ -26,6 +26,12 @@ def decode_bytes(B, H, H_kv, M, D, elt, out_elt=None, include_qo=False):
         return kv
     out_elt = elt if out_elt is None else out_elt
     return kv + B * H * D * elt + B * H * D * out_elt
+
+
+def paged_decode_bytes(lengths, H_kv, D, elt):
+    """KV bytes one paged decode call must read: each sequence's own cached
+    keys only (n = kv_len[b], one layer), summed over the batch."""
+    return sum(kv_cache_bytes(1, max(0, int(n)), H_kv, D, 1, elt) for n in lengths)
 
 
 def visible_pairs(N, M, causal=False, lengths=None):

@@ -59,6 +59,8 @@ struct DecCfg {
   static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16;  // LDS row stride (fp32 rows padded)
   static constexpr int VBYTES = KC * ROWB;            // LDS bytes of one wave's V chunk
   static constexpr int VLOADS = KC * CPR / 64;        // 16-byte V loads per lane per chunk
+  // the rows of one V load instruction lie in one aligned group of 16 keys
+  static_assert(KC % 16 == 0 && 64 % CPR == 0 && 64 / CPR <= 16, "V load rows span a group");
   static constexpr int SPR = DP / 16;                 // 32-byte segments per bf16 row
   static constexpr int SWZ = (SPR < 8 ? SPR : 8) - 1;
   // Registers of one chunk's loads; when two chunks fit, the next chunk is
@@ -90,8 +92,10 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
   }
 }
 
-// EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is given.
-template <bool BF16, int DP, bool EXACT, bool MASKED, bool OUTF32>
+// EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is
+// given.  PAGED: K/V rows are found through a block table and each sequence
+// has its own length.
+template <bool BF16, int DP, bool EXACT, bool MASKED, bool PAGED, bool OUTF32>
 __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs a) {
   using C = DecCfg<BF16, DP>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
@@ -116,11 +120,29 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
 
   const int s = blockIdx.y;
   const int k_begin = s * a.keys_per_split;
-  const int k_end = min(M, k_begin + a.keys_per_split);
+  int k_end = min(M, k_begin + a.keys_per_split);
+  if constexpr (PAGED) k_end = min(k_end, max(0, a.kv_len[b]));   // this sequence's keys
 
-  const size_t kv_base = ((size_t)b * a.H_kv + j) * (size_t)M * D;  // elements
+  // K/V rows are addressed per aligned group of 16 keys.  `group_off(g16)`
+  // is the byte offset of the row of key g16 (a multiple of 16) inside the
+  // K or V buffer; the other 15 keys of the group follow it contiguously.
+  // The group start is wave-uniform, so a paged lookup is one scalar load.
+  const size_t kv_base = PAGED ? 0 : ((size_t)b * a.H_kv + j) * (size_t)M * D;  // elements
   const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
   const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
+  const int32_t* __restrict__ btab = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
+  auto group_off = [&](int g16) -> size_t {
+    if constexpr (PAGED) {
+      const int blk = g16 / a.block_size;
+      // a block id outside the pool is clamped into it: memory stays safe,
+      // the values are then the caller's responsibility
+      const int phys = min(max(btab[blk], 0), a.num_blocks - 1);
+      return (((size_t)phys * a.H_kv + j) * a.block_size + (g16 - blk * a.block_size)) *
+             (size_t)D * C::ELT;
+    } else {
+      return (size_t)g16 * D * C::ELT;
+    }
+  };
   const uint8_t* mrow = MASKED ? a.mask + (size_t)b * M : nullptr;
 
   // 1/sqrt(D) folded with log2(e): p = 2^(s*sl - m*sl).
@@ -158,10 +180,21 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   // to -inf later (K).
   auto load_chunk = [&](int base) {
     Chunk ch;
+    // group kb of the chunk starts at key base + 16 kb; a group wholly past
+    // the split is redirected to the split's last group (its rows are
+    // masked out later, only the addresses must stay valid)
+    const int glast = klast & ~15;
+    int g16[C::NKB];
+    size_t goff[C::NKB];
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
-      const int key = min(base + 16 * kb + c16, klast);
-      const char* krow = kp + (size_t)key * D * C::ELT;
+      g16[kb] = min(base + 16 * kb, glast);
+      goff[kb] = group_off(g16[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      const int key = min(g16[kb] + c16, klast);
+      const char* krow = kp + goff[kb] + (size_t)(key - g16[kb]) * D * C::ELT;
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
         const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
@@ -173,15 +206,19 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
         }
       }
     }
+    // one V load instruction covers 64 / CPR (<= 16) rows of one group
 #pragma unroll
     for (int it = 0; it < C::VLOADS; ++it) {
+      constexpr int RPI = 64 / C::CPR;
+      const int grp = (it * RPI) / 16;
       const int piece = it * 64 + lane;
       const int row = piece / C::CPR;
       const int chunk = piece - row * C::CPR;
       const int key = base + row;
       const int d0 = chunk * (16 / C::ELT);
       const bool ok = key < k_end && (EXACT || d0 < D);
-      const u32x4 x = ld16(vp + ((size_t)min(key, klast) * D + (ok ? d0 : 0)) * C::ELT);
+      const size_t roff = goff[grp] + (size_t)(min(key, klast) - g16[grp]) * D * C::ELT;
+      const u32x4 x = ld16(vp + roff + (size_t)(ok ? d0 : 0) * C::ELT);
       ch.v[it] = sel16(ok, x);
     }
     return ch;
@@ -394,12 +431,13 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
 template <bool BF16, int DP, bool EXACT, bool OUTF32>
 hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * a.head_chunks;
-  if (a.mask) {
-    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, true, OUTF32>), dim3(units, a.splits),
-                       dim3(kThreads), 0, stream, a);
+  const dim3 grid(units, a.splits);
+  if (a.block_table) {  // the paged form takes no mask
+    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+  } else if (a.mask) {
+    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, true, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, OUTF32>), dim3(units, a.splits),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;

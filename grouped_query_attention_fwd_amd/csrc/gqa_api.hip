@@ -66,7 +66,8 @@ const char* gqa_status_string(gqa_status_t s) {
     case GQA_ERR_GROUP: return "H is not a multiple of H_kv";
     case GQA_ERR_DTYPE: return "unsupported dtype combination";
     case GQA_ERR_ALIGN: return "q/k/v/out/workspace must be 16-byte aligned";
-    case GQA_ERR_UNSUPPORTED: return "unsupported head_dim (need D <= 256 and D*sizeof(dtype) % 16 == 0)";
+    case GQA_ERR_UNSUPPORTED:
+      return "unsupported size (need D <= 256, D*sizeof(dtype) % 16 == 0 and, paged, block_size % 16 == 0)";
     case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case GQA_ERR_HIP: return "HIP runtime error";
     case GQA_ERR_ALIAS: return "out overlaps an input or the workspace";
@@ -102,6 +103,63 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
 
   gqa::DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
+  a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
+  a.g = H / H_kv;
+  a.head_chunks = plan.head_chunks;
+  a.splits = plan.splits;
+  a.keys_per_split = plan.keys_per_split;
+  a.in_bf16 = in_dtype == GQA_BF16;
+  a.out_f32 = out_dtype == GQA_F32;
+  if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
+  if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+size_t gqa_decode_paged_workspace_size(int B, int H, int H_kv, int max_blocks, int block_size,
+                                       int D) {
+  const long long m = mul_checked({max_blocks, block_size});
+  if (m < 1 || m >= INT_MAX) return 0;
+  return gqa_decode_workspace_size(B, H, H_kv, (int)m, D);
+}
+
+gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* kv_len, void* out,
+                              int B, int H, int H_kv, int max_blocks, int block_size,
+                              int num_blocks, int D, gqa_dtype_t in_dtype,
+                              gqa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (block_table == nullptr || kv_len == nullptr) return GQA_ERR_NULL;
+  if (max_blocks < 1 || block_size < 1 || num_blocks < 1) return GQA_ERR_SHAPE;
+  if (block_size % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  const long long m = mul_checked({max_blocks, block_size});
+  if (m < 1 || m >= INT_MAX) return GQA_ERR_SHAPE;
+  const int M = (int)m;
+  // the per-sequence view is [B, H_kv, M, D]; the pool has its own row count
+  gqa_status_t st = check_common(q, k_pool, v_pool, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  const long long pool_rows = mul_checked({num_blocks, H_kv, block_size});
+  if (pool_rows < 0 || mul_checked({pool_rows, D, 4}) < 0) return GQA_ERR_SHAPE;
+  if (mul_checked({B, max_blocks}) >= INT_MAX) return GQA_ERR_SHAPE;
+  if (((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)kv_len & 3u) != 0) return GQA_ERR_ALIGN;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D);
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GQA_ERR_ALIGN;
+  }
+  const size_t ein = dtype_size(in_dtype), eout = dtype_size(out_dtype);
+  const size_t qb = (size_t)B * H * D * ein, poolb = (size_t)pool_rows * D * ein;
+  const size_t ob = (size_t)B * H * D * eout;
+  if (overlaps(out, ob, q, qb) || overlaps(out, ob, k_pool, poolb) ||
+      overlaps(out, ob, v_pool, poolb) ||
+      overlaps(out, ob, block_table, (size_t)B * max_blocks * 4) ||
+      overlaps(out, ob, kv_len, (size_t)B * 4) ||
+      (plan.workspace_bytes > 0 && overlaps(out, ob, workspace, plan.workspace_bytes)))
+    return GQA_ERR_ALIAS;
+
+  gqa::DecodeArgs a{};
+  a.q = q; a.k = k_pool; a.v = v_pool; a.mask = nullptr; a.out = out;
+  a.block_table = block_table; a.kv_len = kv_len;
+  a.num_blocks = num_blocks; a.block_size = block_size; a.max_blocks = max_blocks;
   a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
   a.g = H / H_kv;
   a.head_chunks = plan.head_chunks;

@@ -16,6 +16,12 @@ struct DecodeArgs {
   const uint8_t* mask;  // [B, 1, M] or null
   void* out;
   float* partials;      // [units][splits][16][D + 2] fp32, or null when splits == 1
+  // paged KV (block_table != null): k/v are pools [num_blocks][H_kv][block_size][D];
+  // key j of sequence b lives in block block_table[b * max_blocks + j / block_size]
+  // at row j % block_size, and only keys j < kv_len[b] exist.  M = max_blocks * block_size.
+  const int32_t* block_table;
+  const int32_t* kv_len;
+  int num_blocks, block_size, max_blocks;
   int B, H, H_kv, M, D;
   int g;                // H / H_kv
   int head_chunks;      // ceil(g / 16)

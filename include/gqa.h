@@ -65,7 +65,8 @@ typedef enum {
   GQA_ERR_GROUP = 3,       /* H is not a multiple of H_kv                     */
   GQA_ERR_DTYPE = 4,       /* unknown dtype, or out_dtype not in {in, F32}    */
   GQA_ERR_ALIGN = 5,       /* q/k/v/out/workspace not 16-byte aligned         */
-  GQA_ERR_UNSUPPORTED = 6, /* D > 256 or D*sizeof(in_dtype) % 16 != 0         */
+  GQA_ERR_UNSUPPORTED = 6, /* D > 256, D*sizeof(in_dtype) % 16 != 0, or a
+                              paged block_size that is not a multiple of 16  */
   GQA_ERR_WORKSPACE = 7,   /* decode workspace missing or too small           */
   GQA_ERR_HIP = 8,         /* the HIP runtime reported a launch error         */
   GQA_ERR_ALIAS = 9        /* out overlaps an input or the workspace          */
@@ -106,6 +107,51 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v,
  * invalid (gqa_decode then reports the size error).
  */
 size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D);
+
+/*
+ * Paged decode: the decode above over a KV cache kept in fixed-size blocks,
+ * with one cache length per sequence.  This is the serving form of the
+ * KV cache whose per-sequence size the grouping shrinks ("Grouped-Query
+ * Attention vs Multi-Head Attention: Understanding GQA Implementation",
+ * sections on the KV-cache buffers and *Summary*; "Multi-Query Attention",
+ * *Theory* on the decode step re-reading the cache).
+ *
+ *   q           [B, H, 1, D]                          in_dtype
+ *   k_pool,
+ *   v_pool      [num_blocks, H_kv, block_size, D]     in_dtype
+ *   block_table [B, max_blocks] int32: block_table[b][t] is the pool block
+ *               that holds keys t*block_size ... (t+1)*block_size - 1 of
+ *               sequence b
+ *   kv_len      [B] int32: sequence b has keys 0 .. kv_len[b]-1 (values are
+ *               clamped to [0, max_blocks*block_size]; entries of the table
+ *               past the last used block are never read)
+ *   out         [B, H, 1, D]                          out_dtype
+ *   workspace   at least gqa_decode_paged_workspace_size(...) bytes, with
+ *               the same rules as for gqa_decode
+ * Key t of sequence b and KV head j is row
+ *   k_pool[block_table[b][t / block_size], j, t % block_size, :].
+ * A sequence with kv_len[b] == 0 sees no key and yields NaN.  The result
+ * equals gqa_decode over the gathered cache [B, H_kv, max_blocks*block_size,
+ * D] with mask[b][0][t] = (t < kv_len[b]).
+ * Supported: block_size a positive multiple of 16 (else
+ * GQA_ERR_UNSUPPORTED); the limits of gqa_decode with M = max_blocks *
+ * block_size; block_table and kv_len are device memory, 4-byte aligned.
+ * Block ids are trusted: an id outside [0, num_blocks) is clamped into that
+ * range (memory stays in bounds, the result is then meaningless).  Several
+ * sequences may share a block.  No mask argument: kv_len is the visibility.
+ */
+gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* kv_len,
+                              void* out, int B, int H, int H_kv, int max_blocks,
+                              int block_size, int num_blocks, int D,
+                              gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Bytes of paged-decode workspace; equal to gqa_decode_workspace_size(B, H,
+ * H_kv, max_blocks * block_size, D), 0 for invalid sizes. */
+size_t gqa_decode_paged_workspace_size(int B, int H, int H_kv, int max_blocks,
+                                       int block_size, int D);
 
 /*
  * Prefill: N query positions per (batch row, head) against M keys, with an

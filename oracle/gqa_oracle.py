@@ -22,6 +22,12 @@ What it computes, and where each step comes from:
   implementation*: self-attention with a causal mask.  Causal visibility is
   read as "key j is visible to query i iff j <= i" for any N and M
   (top-left aligned), combined with an explicit mask by logical AND.
+* "Grouped-Query Attention vs Multi-Head Attention: Understanding GQA
+  Implementation", KV-cache buffers and *Summary*: at decode time each
+  sequence attends to the keys it has cached so far, stored per KV head.
+  `gather_paged` / `gqa_paged` read such a cache kept in fixed-size blocks
+  through a per-sequence block table, with one cached length per sequence:
+  the result is plain attention over that sequence's first kv_len keys.
 
 The page's recipe yields NaN for a query row that sees no key (softmax over an
 empty set: -inf minus -inf); the oracle keeps that NaN on purpose.
@@ -43,7 +49,7 @@ import math
 import numpy as np
 
 __all__ = ["validate_shapes", "group_size", "expand_kv", "visibility",
-           "attention_weights", "gqa"]
+           "attention_weights", "gqa", "gather_paged", "gqa_paged"]
 
 
 def validate_shapes(q, k, v, mask=None):
@@ -128,3 +134,41 @@ def gqa(q, k, v, mask=None, causal=False):
         vb = expand_kv(np.asarray(v[b:b + 1], dtype=np.float64), g)[0]  # [H, M, D]
         out[b] = np.matmul(w, vb)
     return out
+
+
+def gather_paged(k_pool, v_pool, block_table, kv_len):
+    """Rebuild the contiguous per-sequence cache from a block pool.
+
+    k_pool, v_pool: [num_blocks, H_kv, block_size, D]; block_table
+    [B, max_blocks] of block ids; kv_len [B].  Key t of sequence b and KV
+    head j is k_pool[block_table[b, t // block_size], j, t % block_size].
+    Returns k, v [B, H_kv, max_blocks * block_size, D] (float64, zero past
+    the sequence's length) and the decode mask [B, 1, M] with
+    mask[b, 0, t] = t < kv_len[b] (lengths clamped to [0, M])."""
+    k_pool = np.asarray(k_pool, dtype=np.float64)
+    v_pool = np.asarray(v_pool, dtype=np.float64)
+    table = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(kv_len, dtype=np.int64)
+    num_blocks, H_kv, bs, D = k_pool.shape
+    B, max_blocks = table.shape
+    M = max_blocks * bs
+    k = np.zeros((B, H_kv, M, D))
+    v = np.zeros((B, H_kv, M, D))
+    mask = np.zeros((B, 1, M), dtype=bool)
+    for b in range(B):
+        n = min(max(int(lens[b]), 0), M)
+        for t in range(n):
+            blk = int(table[b, t // bs])
+            if not 0 <= blk < num_blocks:
+                raise ValueError("block id outside the pool")
+            k[b, :, t, :] = k_pool[blk, :, t % bs, :]
+            v[b, :, t, :] = v_pool[blk, :, t % bs, :]
+            mask[b, 0, t] = True
+    return k, v, mask
+
+
+def gqa_paged(q, k_pool, v_pool, block_table, kv_len):
+    """Decode (q [B, H, 1, D]) over a paged cache: gqa() on the gathered
+    cache with the length mask."""
+    k, v, mask = gather_paged(k_pool, v_pool, block_table, kv_len)
+    return gqa(q, k, v, mask)

@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 
 # fake, 16-byte aligned, non-overlapping "device" addresses: never dereferenced
 # because every call below fails validation first
-Q, K, V, O, W, MK = (0x10000000 * (i + 1) for i in range(6))
+Q, K, V, O, W, MK, BT, KL = (0x10000000 * (i + 1) for i in range(8))
 
 
 def declared_functions():
@@ -34,8 +34,8 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared_functions()
-    assert names == ["gqa_decode", "gqa_decode_workspace_size", "gqa_prefill",
-                     "gqa_status_string"]
+    assert names == ["gqa_decode", "gqa_decode_paged", "gqa_decode_paged_workspace_size",
+                     "gqa_decode_workspace_size", "gqa_prefill", "gqa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", gqa.library_path()],
@@ -62,7 +62,17 @@ def pre(lib, q=Q, k=K, v=V, mask=None, causal=0, out=O, B=2, H=8, H_kv=2, N=7, M
     return lib.gqa_prefill(q, k, v, mask, causal, out, B, H, H_kv, N, M, D, tin, tout, None)
 
 
-@pytest.mark.parametrize("fn", [dec, pre])
+def paged(lib, q=Q, k=K, v=V, bt=BT, kl=KL, out=O, B=2, H=8, H_kv=2, M=None, D=128,
+          tin=BF16, tout=BF16, ws=W, wsb=1 << 30, max_blocks=None, block_size=32,
+          num_blocks=64):
+    # M, when given, is split into max_blocks blocks of block_size keys
+    if max_blocks is None:
+        max_blocks = 10 if M is None else (M if M < 1 else max(1, M // block_size))
+    return lib.gqa_decode_paged(q, k, v, bt, kl, out, B, H, H_kv, max_blocks, block_size,
+                                num_blocks, D, tin, tout, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", [dec, pre, paged])
 def test_rejections_common(lib, fn):
     assert fn(lib, q=None) == NULL
     assert fn(lib, k=None) == NULL
@@ -103,6 +113,28 @@ def test_rejections_decode_workspace(lib):
     assert dec(lib, out=W, wsb=need) == ALIAS
 
 
+def test_rejections_paged(lib):
+    assert paged(lib, bt=None) == NULL
+    assert paged(lib, kl=None) == NULL
+    assert paged(lib, max_blocks=0) == SHAPE
+    assert paged(lib, block_size=0) == SHAPE
+    assert paged(lib, num_blocks=0) == SHAPE
+    assert paged(lib, num_blocks=-1) == SHAPE
+    assert paged(lib, block_size=24) == UNSUP             # not a multiple of 16
+    assert paged(lib, block_size=8) == UNSUP
+    assert paged(lib, max_blocks=1 << 20, block_size=1 << 12) == SHAPE  # M >= 2^31
+    assert paged(lib, bt=BT + 2) == ALIGN
+    assert paged(lib, kl=KL + 1) == ALIGN
+    assert paged(lib, out=BT) == ALIAS
+    assert paged(lib, out=KL) == ALIAS
+    need = lib.gqa_decode_paged_workspace_size(2, 8, 2, 10, 32, 128)
+    assert need == lib.gqa_decode_workspace_size(2, 8, 2, 320, 128) > 0
+    assert paged(lib, ws=None, wsb=0) == WS
+    assert paged(lib, wsb=need - 1) == WS
+    assert lib.gqa_decode_paged_workspace_size(2, 8, 2, 0, 32, 128) == 0
+    assert lib.gqa_decode_paged_workspace_size(2, 8, 2, 1 << 20, 1 << 12, 128) == 0
+
+
 def test_workspace_size_rules(lib):
     f = lib.gqa_decode_workspace_size
     assert f(0, 8, 2, 64, 128) == 0
@@ -123,3 +155,6 @@ def test_binding_fails_loudly_without_gpu_tensors():
         gqa.decode(q, q[:, :2], q[:, :2])
     with pytest.raises(ValueError):
         gqa.prefill(q, q[:, :2], q[:, :2])
+    bt = torch.zeros(1, 1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        gqa.decode_paged(q, q[:, :2], q[:, :2], bt, bt[0])

@@ -33,6 +33,13 @@ def test_decode_workload_bytes():
     assert accounting.decode_bytes(16, 64, 8, 32768, 128, 2) == 2147483648
 
 
+def test_paged_decode_bytes():
+    # equal lengths reduce to the contiguous count; negative lengths read nothing
+    assert accounting.paged_decode_bytes([4096] * 16, 8, 128, 2) == \
+        accounting.decode_bytes(16, 32, 8, 4096, 128, 2)
+    assert accounting.paged_decode_bytes([10, 0, -3, 5], 2, 8, 4) == 2 * 15 * 2 * 8 * 4
+
+
 def test_visible_pairs_brute_force():
     for N, M in [(1, 1), (5, 5), (4, 9), (9, 4), (33, 17)]:
         brute = sum(1 for i in range(N) for j in range(M) if j <= i)

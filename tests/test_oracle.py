@@ -72,6 +72,50 @@ def brute_force(q, k, v, mask=None, causal=False):
     return out
 
 
+def rand_paged(seed, B, H, H_kv, D, bs, lens, max_blocks, slack=3):
+    """Random pool, a random block assignment (blocks shuffled over the pool,
+    unused table entries -1) and the given lengths."""
+    r = rng(seed)
+    need = [-(-min(n, max_blocks * bs) // bs) for n in lens]
+    nb = sum(need) + slack
+    q = r.standard_normal((B, H, 1, D))
+    kp = r.standard_normal((nb, H_kv, bs, D))
+    vp = r.standard_normal((nb, H_kv, bs, D))
+    perm = r.permutation(nb)
+    table = -np.ones((B, max_blocks), dtype=np.int64)
+    at = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[at:at + need[b]]
+        at += need[b]
+    return q, kp, vp, table, np.asarray(lens)
+
+
+def brute_force_paged(q, kp, vp, table, lens):
+    """Pure-Python decode over a paged cache, indexing the pool per key."""
+    B, H, _, D = q.shape
+    H_kv, bs = kp.shape[1], kp.shape[2]
+    g = H // H_kv
+    out = np.zeros((B, H, 1, D))
+    for b in range(B):
+        for h in range(H):
+            j = h // g
+            s = []
+            for t in range(int(lens[b])):
+                blk, off = int(table[b][t // bs]), t % bs
+                dot = sum(float(q[b, h, 0, d]) * float(kp[blk, j, off, d]) for d in range(D))
+                s.append(((blk, off), dot / math.sqrt(D)))
+            if not s:
+                out[b, h, 0, :] = float("nan")
+                continue
+            mx = max(x for _, x in s)
+            w = [(loc, math.exp(x - mx)) for loc, x in s]
+            tot = sum(x for _, x in w)
+            for d in range(D):
+                out[b, h, 0, d] = sum(x * float(vp[blk, j, off, d])
+                                      for (blk, off), x in w) / tot
+    return out
+
+
 # ---------------------------------------------------------------- pin suite
 # Each pin takes an oracle module and raises AssertionError (or any error)
 # when the module disagrees with what the pages and the mathematics fix.
@@ -309,12 +353,71 @@ def pin_rejects_bad_group(orc):
         orc.gqa(q, k, v)
 
 
+def pin_paged_brute_force(orc):
+    """Paged decode equals per-key brute force over the pool (empty
+    sequence -> NaN, lengths ending mid-block, block ids shuffled)."""
+    q, kp, vp, table, lens = rand_paged(60, 4, 6, 2, 4, 3, [7, 0, 9, 1], max_blocks=4)
+    got = orc.gqa_paged(q, kp, vp, table, lens)
+    ref = brute_force_paged(q, kp, vp, table, lens)
+    assert np.isnan(got[1]).all()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_paged_identity_table(orc):
+    """A contiguous cache cut into blocks in order, with full lengths, is
+    the unpaged decode exactly."""
+    B, H, H_kv, M, D, bs = 2, 8, 2, 12, 4, 4
+    q, k, v = rand_qkv(61, B, H, H_kv, 1, M, D)
+    mb = M // bs
+    # [B, H_kv, mb, bs, D] -> [B, mb, H_kv, bs, D] -> pool [B*mb, H_kv, bs, D]
+    kp = k.reshape(B, H_kv, mb, bs, D).transpose(0, 2, 1, 3, 4).reshape(B * mb, H_kv, bs, D)
+    vp = v.reshape(B, H_kv, mb, bs, D).transpose(0, 2, 1, 3, 4).reshape(B * mb, H_kv, bs, D)
+    table = np.arange(B * mb).reshape(B, mb)
+    got = orc.gqa_paged(q, kp, vp, table, np.full(B, M))
+    assert np.array_equal(got, orc.gqa(q, k, v))
+
+
+def pin_paged_length_is_truncation(orc):
+    """Only the first kv_len keys count: equal to the unpaged decode of the
+    truncated cache, for lengths inside and at the end of blocks."""
+    B, H, H_kv, M, D, bs = 3, 4, 2, 16, 4, 4
+    q, k, v = rand_qkv(62, B, H, H_kv, 1, M, D)
+    mb = M // bs
+    kp = k.reshape(B, H_kv, mb, bs, D).transpose(0, 2, 1, 3, 4).reshape(B * mb, H_kv, bs, D)
+    vp = v.reshape(B, H_kv, mb, bs, D).transpose(0, 2, 1, 3, 4).reshape(B * mb, H_kv, bs, D)
+    table = np.arange(B * mb).reshape(B, mb)
+    lens = [5, 16, 8]
+    got = orc.gqa_paged(q, kp, vp, table, lens)
+    for b, n in enumerate(lens):
+        ref = orc.gqa(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n])
+        np.testing.assert_allclose(got[b:b + 1], ref, rtol=1e-13, atol=1e-14)
+
+
+def pin_paged_block_permutation(orc):
+    """Moving blocks around the pool and renaming them in the table changes
+    nothing, bit for bit; a shared block serves two sequences."""
+    q, kp, vp, table, lens = rand_paged(63, 2, 4, 2, 4, 4, [10, 6], max_blocks=3)
+    table[1, 0] = table[0, 0]                 # sequence 1 shares sequence 0's first block
+    base = orc.gqa_paged(q, kp, vp, table, lens)
+    perm = rng(64).permutation(kp.shape[0])   # new position of each block
+    kp2 = np.empty_like(kp)
+    vp2 = np.empty_like(vp)
+    kp2[perm] = kp
+    vp2[perm] = vp
+    table2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    assert np.array_equal(orc.gqa_paged(q, kp2, vp2, table2, lens), base)
+    shared = brute_force_paged(q, kp, vp, table, lens)
+    np.testing.assert_allclose(base, shared, rtol=1e-12, atol=1e-13)
+
+
 PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
         pin_mha_equals_per_head, pin_mqa_brute_force, pin_single_key,
         pin_two_keys_closed_form, pin_scale_exact, pin_zero_keys_give_mean,
         pin_head_mapping_exact, pin_weights_sum_to_one,
         pin_masked_keys_contribute_nothing, pin_causal_properties,
-        pin_key_permutation, pin_empty_row_is_nan, pin_rejects_bad_group]
+        pin_key_permutation, pin_empty_row_is_nan, pin_rejects_bad_group,
+        pin_paged_brute_force, pin_paged_identity_table, pin_paged_length_is_truncation,
+        pin_paged_block_permutation]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -358,6 +461,11 @@ MUTANTS = {
     "mask_ignored": (r"vis &= np\.asarray\(mask, dtype=bool\)", "pass"),
     "transposed_v": (r"out\[b\] = np\.matmul\(w, vb\)",
                      "out[b] = np.matmul(w, vb.transpose(0, 2, 1)[:, :w.shape[-1], :]) if vb.shape[1] == vb.shape[2] else np.matmul(w, vb)[..., ::-1]"),
+    "paged_row_offset": (r"k_pool\[blk, :, t % bs, :\]", "k_pool[blk, :, (t + 1) % bs, :]"),
+    "paged_block_index": (r"table\[b, t // bs\]", "table[b, t % max_blocks]"),
+    "paged_length_inclusive": (r"for t in range\(n\):", "for t in range(min(n + 1, M)):"),
+    "paged_v_from_k": (r"v\[b, :, t, :\] = v_pool", "v[b, :, t, :] = k_pool"),
+    "paged_head_ignored": (r"k\[b, :, t, :\] = k_pool\[blk, :,", "k[b, :, t, :] = k_pool[blk, :1,"),
 }
 
 

@@ -27,7 +27,9 @@ import dataclasses
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "make_inputs", "random_case"]
+__all__ = ["Workload", "WORKLOADS", "by_name", "make_inputs", "random_case",
+           "PagedWorkload", "PAGED_WORKLOADS", "paged_by_name", "make_paged_inputs",
+           "random_paged_case"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -129,3 +131,95 @@ def random_case(seed, B, H, H_kv, N, M, D, dtype=torch.float32,
     elif mask_kind is not None:
         raise ValueError(mask_kind)
     return q, k, v, mask
+
+
+# ------------------------------------------------------------ paged KV cache
+@dataclasses.dataclass(frozen=True)
+class PagedWorkload:
+    """Decode over a KV cache kept in blocks of ``block_size`` keys.
+
+    Each of the B sequences has its own cached length; ``lengths`` is
+    "full" (every sequence holds max_len keys) or "uniform" (length drawn
+    uniformly from {1, ..., max_len}).  Blocks are scattered over the pool
+    in a random order."""
+    name: str
+    seed: int
+    B: int
+    H: int
+    H_kv: int
+    max_len: int
+    D: int
+    block_size: int
+    dtype: str
+    lengths: str = "uniform"
+
+    @property
+    def max_blocks(self) -> int:
+        return -(-self.max_len // self.block_size)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+
+PAGED_WORKLOADS = [
+    # the Mistral-7B-shaped decode batch with serving-style mixed lengths
+    PagedWorkload("decode_paged_mistral7b_varlen", 6, 16, 32, 8, 4096, 128, 16, "bf16"),
+    # the same batch with every sequence full: same bytes as the contiguous decode
+    PagedWorkload("decode_paged_mistral7b_full", 7, 16, 32, 8, 4096, 128, 16, "bf16",
+                  lengths="full"),
+]
+
+
+def paged_by_name(name: str) -> PagedWorkload:
+    for w in PAGED_WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def random_paged_case(seed, B, H, H_kv, D, block_size, max_len, dtype=torch.float32,
+                      lengths="uniform", slack_blocks=3, shared_first_block=False,
+                      q_scale=1.0):
+    """(q, k_pool, v_pool, block_table, kv_len) as CPU tensors.
+
+    Draw order: q [B,H,1,D], then the pool K and V [num_blocks, H_kv,
+    block_size, D] as float32 N(0,1) (cast afterwards for bf16), then the
+    lengths, then a random permutation that scatters the blocks.  lengths:
+    "uniform" (U{1..max_len}), "full", or an explicit list (0 allowed).
+    Table entries past a sequence's last block are -1 (never read).
+    shared_first_block: sequence 1 reuses sequence 0's first block (a shared
+    prefix), which is legal."""
+    gen = torch.Generator().manual_seed(seed)
+    max_blocks = -(-max_len // block_size)
+    if isinstance(lengths, str):
+        probe = torch.Generator().manual_seed(seed + 1_000_003)
+        if lengths == "full":
+            lens = torch.full((B,), max_len, dtype=torch.int64)
+        elif lengths == "uniform":
+            lens = torch.randint(1, max_len + 1, (B,), generator=probe)
+        else:
+            raise ValueError(lengths)
+    else:
+        lens = torch.tensor(list(lengths), dtype=torch.int64)
+    need = [-(-int(n) // block_size) for n in lens]
+    num_blocks = sum(need) + slack_blocks
+    q = torch.randn((B, H, 1, D), generator=gen, dtype=torch.float32) * q_scale
+    kp = torch.randn((num_blocks, H_kv, block_size, D), generator=gen, dtype=torch.float32)
+    vp = torch.randn((num_blocks, H_kv, block_size, D), generator=gen, dtype=torch.float32)
+    if dtype == torch.bfloat16:
+        q, kp, vp = q.to(dtype), kp.to(dtype), vp.to(dtype)
+    perm = torch.randperm(num_blocks, generator=gen)
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    at = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[at:at + need[b]].to(torch.int32)
+        at += need[b]
+    if shared_first_block and B > 1 and need[0] > 0 and need[1] > 0:
+        table[1, 0] = table[0, 0]
+    return q, kp, vp, table, lens.to(torch.int32)
+
+
+def make_paged_inputs(w: PagedWorkload):
+    return random_paged_case(w.seed, w.B, w.H, w.H_kv, w.D, w.block_size, w.max_len,
+                             w.torch_dtype, lengths=w.lengths, slack_blocks=0)
