@@ -46,6 +46,9 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #ifndef GQA_DECODE_TARGET_WGS
 #define GQA_DECODE_TARGET_WGS 256
 #endif
+#ifndef GQA_DECODE_PAGED_TARGET_WGS
+#define GQA_DECODE_PAGED_TARGET_WGS 256
+#endif
 
 template <bool BF16, int DP>
 struct DecCfg {
@@ -107,18 +110,26 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   const int c16 = lane & 15;
   const int qg = lane >> 4;
 
-  const int unit = blockIdx.x;
+  // Units are numbered (b, KV head, head chunk).  With xcd_group the
+  // workgroups are renumbered so that the head chunks of one (b, KV head),
+  // which stream the same K/V rows, run side by side on one XCD (workgroup
+  // L goes to XCD L % 8), where the later reader can find rows in L2.
+  int unit = blockIdx.x;
+  const int s = blockIdx.y;
+  if (a.xcd_group) {
+    const int x = unit & 7, i = unit >> 3;
+    unit = ((i / a.head_chunks) * 8 + x) * a.head_chunks + i % a.head_chunks;
+  }
   const int per_b = a.H_kv * a.head_chunks;
   const int b = unit / per_b;
   const int rem = unit - b * per_b;
   const int j = rem / a.head_chunks;
   const int hc = rem - j * a.head_chunks;
-  const int h0 = j * a.g + hc * 16;
-  const int gh = min(16, a.g - hc * 16);
+  const int h0 = j * a.g + hc * a.head_chunk;
+  const int gh = min(a.head_chunk, a.g - hc * a.head_chunk);
   const int D = EXACT ? DP : a.D;
   const int M = a.M;
 
-  const int s = blockIdx.y;
   const int k_begin = s * a.keys_per_split;
   int k_end = min(M, k_begin + a.keys_per_split);
   if constexpr (PAGED) k_end = min(k_end, max(0, a.kv_len[b]));   // this sequence's keys
@@ -397,7 +408,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
 // in split order.  One thread per output element; blockIdx.y walks the
 // (head, d) elements of a unit in blocks of kMergeThreads.
 constexpr int kMergeThreads = 128;
-template <bool OUTF32>
+// MAXS > 0: at most MAXS splits; every partial is loaded up front (indexes
+// clamped to the last split) so the loads overlap.  MAXS == 0: any count.
+template <bool OUTF32, int MAXS>
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int per_b = a.H_kv * a.head_chunks;
@@ -405,8 +418,8 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int rem = unit - b * per_b;
   const int j = rem / a.head_chunks;
   const int hc = rem - j * a.head_chunks;
-  const int h0 = j * a.g + hc * 16;
-  const int gh = min(16, a.g - hc * 16);
+  const int h0 = j * a.g + hc * a.head_chunk;
+  const int gh = min(a.head_chunk, a.g - hc * a.head_chunk);
   const int D = a.D;
   const int idx = blockIdx.y * kMergeThreads + threadIdx.x;
   if (idx >= gh * D) return;
@@ -414,16 +427,40 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int d = idx - hh * D;
   const float sl = kLog2e / sqrtf((float)D);
   const size_t stride = 16 * (size_t)(D + 2);
-  const float* ph = a.partials + (size_t)unit * a.splits * stride + (size_t)hh * (D + 2);
-  float mx = kNegInf;
-  for (int ss = 0; ss < a.splits; ++ss) mx = fmaxf(mx, ph[ss * stride]);
-  const float mu = (mx == kNegInf) ? 0.f : mx;
+  const int S = a.splits;
+  const float* ph = a.partials + (size_t)unit * S * stride + (size_t)hh * (D + 2);
   float L = 0.f, A = 0.f;
-  for (int ss = 0; ss < a.splits; ++ss) {
-    const float* p = ph + ss * stride;
-    const float f = exp2_hw((p[0] - mu) * sl);
-    L = fmaf(p[1], f, L);
-    A = fmaf(p[2 + d], f, A);
+  if constexpr (MAXS > 0) {
+    float pm[MAXS], pl[MAXS], pa[MAXS];
+#pragma unroll
+    for (int ss = 0; ss < MAXS; ++ss) {
+      const float* p = ph + (size_t)min(ss, S - 1) * stride;
+      pm[ss] = p[0];
+      pl[ss] = p[1];
+      pa[ss] = p[2 + d];
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int ss = 0; ss < MAXS; ++ss) mx = fmaxf(mx, pm[ss]);  // clamped copies change nothing
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+#pragma unroll
+    for (int ss = 0; ss < MAXS; ++ss) {
+      if (ss < S) {
+        const float f = exp2_hw((pm[ss] - mu) * sl);
+        L = fmaf(pl[ss], f, L);
+        A = fmaf(pa[ss], f, A);
+      }
+    }
+  } else {
+    float mx = kNegInf;
+    for (int ss = 0; ss < S; ++ss) mx = fmaxf(mx, ph[ss * stride]);
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+    for (int ss = 0; ss < S; ++ss) {
+      const float* p = ph + ss * stride;
+      const float f = exp2_hw((p[0] - mu) * sl);
+      L = fmaf(p[1], f, L);
+      A = fmaf(p[2 + d], f, A);
+    }
   }
   store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
 }
@@ -441,9 +478,15 @@ hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const int per_unit = (min(16, a.g) * a.D + kMergeThreads - 1) / kMergeThreads;
-  hipLaunchKernelGGL((decode_merge_kernel<OUTF32>), dim3(units, per_unit), dim3(kMergeThreads), 0,
-                     stream, a);
+  const int per_unit = (a.head_chunk * a.D + kMergeThreads - 1) / kMergeThreads;
+  const dim3 mgrid(units, per_unit);
+  if (a.splits <= 2) {
+    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 2>), mgrid, dim3(kMergeThreads), 0, stream, a);
+  } else if (a.splits <= 8) {
+    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 8>), mgrid, dim3(kMergeThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 0>), mgrid, dim3(kMergeThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -466,12 +509,20 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int H, int H_kv, int M, int D) {
+DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
   DecodePlan p{};
   const int g = H / H_kv;
-  p.head_chunks = (g + 15) / 16;
-  const long units = (long)B * H_kv * p.head_chunks;
-  const long target_wgs = GQA_DECODE_TARGET_WGS;
+  // At most 16 query heads share one matrix-core tile; larger groups are cut
+  // into equal chunks, each a unit that re-reads the group's K/V rows.
+  const int chunks = (g + 15) / 16;
+  p.head_chunk = (g + chunks - 1) / chunks;
+  p.head_chunks = (g + p.head_chunk - 1) / p.head_chunk;
+  const long kv_units = (long)B * H_kv;
+  p.xcd_group = (p.head_chunks > 1 && kv_units % 8 == 0) ? 1 : 0;
+  const long units = kv_units * p.head_chunks;
+  // With per-sequence lengths the host does not know how long each sequence
+  // is; the paged form has its own target so the two can be tuned apart.
+  const long target_wgs = paged ? GQA_DECODE_PAGED_TARGET_WGS : GQA_DECODE_TARGET_WGS;
   const long max_splits = (M + kRoundKeys - 1) / kRoundKeys;
   long splits = (target_wgs + units - 1) / units;
   if (splits > max_splits) splits = max_splits;

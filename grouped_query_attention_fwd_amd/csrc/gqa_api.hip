@@ -79,7 +79,7 @@ size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D) {
   if (B < 1 || H < 1 || H_kv < 1 || M < 1 || D < 1 || H % H_kv != 0) return 0;
   const long long kvrows = mul_checked({B, H_kv, M});
   if (kvrows < 0 || kvrows >= INT_MAX || mul_checked({B, H}) >= INT_MAX) return 0;
-  return gqa::plan_decode(B, H, H_kv, M, D).workspace_bytes;
+  return gqa::plan_decode(B, H, H_kv, M, D, false).workspace_bytes;
 }
 
 gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8_t* mask,
@@ -88,7 +88,7 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
                         void* stream) {
   gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
   if (st != GQA_OK) return st;
-  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D, false);
   if (plan.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_ALIGN;
@@ -105,7 +105,9 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
   a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
   a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
   a.g = H / H_kv;
+  a.head_chunk = plan.head_chunk;
   a.head_chunks = plan.head_chunks;
+  a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
   a.in_bf16 = in_dtype == GQA_BF16;
@@ -119,7 +121,10 @@ size_t gqa_decode_paged_workspace_size(int B, int H, int H_kv, int max_blocks, i
                                        int D) {
   const long long m = mul_checked({max_blocks, block_size});
   if (m < 1 || m >= INT_MAX) return 0;
-  return gqa_decode_workspace_size(B, H, H_kv, (int)m, D);
+  if (B < 1 || H < 1 || H_kv < 1 || D < 1 || H % H_kv != 0) return 0;
+  const long long kvrows = mul_checked({B, H_kv, m});
+  if (kvrows < 0 || kvrows >= INT_MAX || mul_checked({B, H}) >= INT_MAX) return 0;
+  return gqa::plan_decode(B, H, H_kv, (int)m, D, true).workspace_bytes;
 }
 
 gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
@@ -141,7 +146,7 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   if (pool_rows < 0 || mul_checked({pool_rows, D, 4}) < 0) return GQA_ERR_SHAPE;
   if (mul_checked({B, max_blocks}) >= INT_MAX) return GQA_ERR_SHAPE;
   if (((uintptr_t)block_table & 3u) != 0 || ((uintptr_t)kv_len & 3u) != 0) return GQA_ERR_ALIGN;
-  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D, true);
   if (plan.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return GQA_ERR_ALIGN;
@@ -162,7 +167,9 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   a.num_blocks = num_blocks; a.block_size = block_size; a.max_blocks = max_blocks;
   a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
   a.g = H / H_kv;
+  a.head_chunk = plan.head_chunk;
   a.head_chunks = plan.head_chunks;
+  a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
   a.in_bf16 = in_dtype == GQA_BF16;

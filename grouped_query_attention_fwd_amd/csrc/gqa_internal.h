@@ -24,7 +24,9 @@ struct DecodeArgs {
   int num_blocks, block_size, max_blocks;
   int B, H, H_kv, M, D;
   int g;                // H / H_kv
-  int head_chunks;      // ceil(g / 16)
+  int head_chunk;       // query heads per unit (<= 16)
+  int head_chunks;      // ceil(g / head_chunk): units per (b, KV head)
+  int xcd_group;        // 1: the head chunks of one (b, KV head) share an XCD
   int splits;           // key-range splits per unit
   int keys_per_split;   // multiple of 256
   bool in_bf16;
@@ -47,13 +49,15 @@ struct PrefillArgs {
 // Split plan shared by the workspace query and the decode launch, so both
 // agree for the same shapes.
 struct DecodePlan {
+  int head_chunk;
   int head_chunks;
+  int xcd_group;
   int splits;
   int keys_per_split;
   size_t partials_bytes;
   size_t workspace_bytes;  // 0 when splits == 1
 };
-DecodePlan plan_decode(int B, int H, int H_kv, int M, int D);
+DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

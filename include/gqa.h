@@ -148,8 +148,9 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Bytes of paged-decode workspace; equal to gqa_decode_workspace_size(B, H,
- * H_kv, max_blocks * block_size, D), 0 for invalid sizes. */
+/* Bytes of paged-decode workspace for these sizes (independent of dtype,
+ * of the lengths and of the device); 0 when none is needed or the sizes are
+ * invalid. */
 size_t gqa_decode_paged_workspace_size(int B, int H, int H_kv, int max_blocks,
                                        int block_size, int D);
 

@@ -128,7 +128,7 @@ def test_rejections_paged(lib):
     assert paged(lib, out=BT) == ALIAS
     assert paged(lib, out=KL) == ALIAS
     need = lib.gqa_decode_paged_workspace_size(2, 8, 2, 10, 32, 128)
-    assert need == lib.gqa_decode_workspace_size(2, 8, 2, 320, 128) > 0
+    assert need > 0
     assert paged(lib, ws=None, wsb=0) == WS
     assert paged(lib, wsb=need - 1) == WS
     assert lib.gqa_decode_paged_workspace_size(2, 8, 2, 0, 32, 128) == 0
@@ -141,11 +141,11 @@ def test_workspace_size_rules(lib):
     assert f(1, 6, 4, 64, 128) == 0          # bad group
     # many units: one split per unit, no workspace
     assert f(512, 8, 8, 256, 128) == 0
-    # the Mistral-7B-shaped decode needs splits and therefore a workspace
-    s2 = f(16, 32, 8, 4096, 128)
+    # few (batch row, KV head) pairs and a long cache: key splits, workspace
+    s2 = f(1, 8, 1, 65536, 128)
     assert s2 > 0 and s2 % 4 == 0
-    # independent of the dtype-free arguments' order of calls (pure function)
-    assert f(16, 32, 8, 4096, 128) == s2
+    # a pure function of the sizes
+    assert f(1, 8, 1, 65536, 128) == s2
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
