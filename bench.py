@@ -7,8 +7,10 @@ HBM bandwidth = algorithmic KV bytes / time.  The same run also measures the
 Llama-2-70B-shaped decode (M 32768), the causal bf16 prefill (B4, 32/8 heads,
 N = M = 4096, D 128; TFLOP/s over the visible pairs) and the paged decode of
 the Mistral-shaped batch (blocks of 16 keys scattered over a pool; mixed
-lengths, and all lengths 4096; GB/s over each sequence's own keys), which
-appear under "secondary".
+lengths, and all lengths 4096; GB/s over each sequence's own keys) and two
+banded prefills (a 4096-key sliding window over N = M = 16384, and a
+512-query chunk after 3584 cached keys, bottom-right causal), which appear
+under "secondary".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
                     [--no-cpu-baseline] [--only WORKLOAD]
@@ -100,6 +102,8 @@ def setup(name, torch, copies=1):
     info = {"w": w, "kind": w.kind, "cpu": (q, k, v, mask, causal), "sets": sets}
     if w.kind == "decode":
         info["units"] = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, elt)
+    elif w.band is not None:
+        info["units"] = accounting.band_flops(w.B, w.H, w.N, w.M, w.D, *w.band)
     else:
         lengths = None
         if mask is not None:
@@ -125,6 +129,9 @@ def make_call(info, torch):
                          dtype=torch.uint8, device="cuda")
         for (q, k, v, m) in info["sets"]:
             ops.append(gqa.decode_op(q, k, v, m, workspace=ws))
+    elif w.band is not None:
+        for (q, k, v, m) in info["sets"]:
+            ops.append(gqa.prefill_band_op(q, k, v, m, *w.band))
     else:
         for (q, k, v, m) in info["sets"]:
             ops.append(gqa.prefill_op(q, k, v, m, causal=info["cpu"][4]))
@@ -253,6 +260,9 @@ def result_for(info, timing):
     else:
         config = {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "M": w.M,
                   "D": w.D, "dtype": w.dtype, "causal": w.causal, "padded_mask": w.padded}
+        if w.band is not None:
+            config["band"] = {"q_offset": w.q_offset, "window_left": w.window_left,
+                              "window_right": w.window_right}
     roof["duration_us"] = round(timing["launch_ms_avg"] * 1e3, 2)
     return {
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
@@ -401,7 +411,8 @@ def main():
     names = [primary]
     if not args.skip_secondary and not args.only:
         names += ["decode_llama70b_m32768", "prefill_causal_n4096",
-                  "decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full"]
+                  "decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full",
+                  "prefill_window4096_n16384", "prefill_chunk512_m4096"]
     copies = {"decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1,
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}

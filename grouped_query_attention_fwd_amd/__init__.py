@@ -10,6 +10,10 @@ are not on a GPU the call raises.
         q [B,H,1,D], k/v [B,H_kv,M,D], mask [B,1,M] bool/uint8 or None
     prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None)
         q [B,H,N,D], k/v [B,H_kv,M,D], mask [B,N,M] bool/uint8 or None
+    prefill_band(q, k, v, mask=None, q_offset=0, window_left=-1, window_right=-1,
+                 out=None, out_dtype=None)
+        key j visible to query i iff i+q_offset-window_left <= j <= i+q_offset+window_right
+        (a negative window leaves that side open)
     decode_paged(q, k_pool, v_pool, block_table, kv_len, out=None, out_dtype=None,
                  workspace=None)
         q [B,H,1,D], pools [num_blocks,H_kv,block_size,D], block_table
@@ -28,7 +32,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["decode", "decode_paged", "prefill", "decode_op", "decode_paged_op", "prefill_op",
+__all__ = ["decode", "decode_paged", "prefill", "prefill_band", "decode_op", "decode_paged_op",
+           "prefill_op", "prefill_band_op",
            "decode_workspace_size", "decode_paged_workspace_size", "status_string",
            "library_path", "GQAError", "load_library"]
 
@@ -65,6 +70,8 @@ def load_library():
     lib.gqa_decode.restype = i
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, vp]
     lib.gqa_prefill.restype = i
+    lib.gqa_prefill_band.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, vp]
+    lib.gqa_prefill_band.restype = i
     lib.gqa_decode_workspace_size.argtypes = [i, i, i, i, i]
     lib.gqa_decode_workspace_size.restype = sz
     lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, sz,
@@ -222,6 +229,20 @@ def _prepare_prefill(q, k, v, mask, causal, out, out_dtype):
     return lib, args, out
 
 
+def _prepare_prefill_band(q, k, v, mask, q_offset, window_left, window_right, out, out_dtype):
+    _check_tensors(q, k, v, mask)
+    B, H, N, D = q.shape
+    _, H_kv, M, _ = k.shape
+    if mask is not None and tuple(mask.shape) != (B, N, M):
+        raise ValueError("prefill mask must be [B,N,M]")
+    out = _out(q, out, out_dtype, (B, H, N, D))
+    lib = load_library()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask), out.data_ptr(),
+            B, H, H_kv, N, M, D, int(q_offset), int(window_left), int(window_right),
+            _dtype_code(q.dtype), _dtype_code(out.dtype))
+    return lib, args, out
+
+
 class _PreparedOp:
     """A validated, marshalled call: calling it only passes the current
     stream and enqueues the kernels.  The tensors it was built from must stay
@@ -262,6 +283,14 @@ def prefill_op(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
     return _PreparedOp(lib.gqa_prefill, args, out, (q, k, v, mask))
 
 
+def prefill_band_op(q, k, v, mask=None, q_offset=0, window_left=-1, window_right=-1, out=None,
+                    out_dtype=None):
+    """Prepared banded prefill call; see decode_op."""
+    lib, args, out = _prepare_prefill_band(q, k, v, mask, q_offset, window_left, window_right,
+                                           out, out_dtype)
+    return _PreparedOp(lib.gqa_prefill_band, args, out, (q, k, v, mask))
+
+
 def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
     """One decode step; see the module docstring.  workspace: optional
     uint8 device tensor of at least decode_workspace_size(...) bytes (no
@@ -292,4 +321,19 @@ def prefill(q, k, v, mask=None, causal=False, out=None, out_dtype=None):
     lib, args, out = _prepare_prefill(q, k, v, mask, causal, out, out_dtype)
     with torch.cuda.device(q.device):
         _check(lib.gqa_prefill(*args, torch.cuda.current_stream(q.device).cuda_stream))
+    return out
+
+
+def prefill_band(q, k, v, mask=None, q_offset=0, window_left=-1, window_right=-1, out=None,
+                 out_dtype=None):
+    """Prefill with each query's keys limited to a band around its position
+    i + q_offset: window_left keys before it and window_right keys after it
+    (negative = unbounded).  Causal is window_right=0; q_offset=M-N places
+    the queries at the end of the keys; window_left=W-1, window_right=0 is a
+    sliding window of W keys."""
+    torch = _torch()
+    lib, args, out = _prepare_prefill_band(q, k, v, mask, q_offset, window_left, window_right,
+                                           out, out_dtype)
+    with torch.cuda.device(q.device):
+        _check(lib.gqa_prefill_band(*args, torch.cuda.current_stream(q.device).cuda_stream))
     return out

@@ -9,7 +9,7 @@ kv_cache_bytes is the KV-cache equation of the *Theory* section of
 from __future__ import annotations
 
 __all__ = ["kv_cache_bytes", "decode_bytes", "paged_decode_bytes", "visible_pairs",
-           "prefill_flops", "DTYPE_BYTES"]
+           "band_pairs", "prefill_flops", "band_flops", "DTYPE_BYTES"]
 
 DTYPE_BYTES = {"fp32": 4, "bf16": 2}
 
@@ -56,3 +56,21 @@ def prefill_flops(B, H, N, M, D, causal=False, lengths=None):
     if lengths is None:
         return 4 * D * H * B * vp
     return 4 * D * H * sum(vp)
+
+
+def band_pairs(N, M, q_offset=0, window_left=-1, window_right=-1):
+    """Visible (query, key) pairs per (batch row, head) for the band
+    i + q_offset - window_left <= j <= i + q_offset + window_right
+    (negative window = open side), keys in [0, M)."""
+    total = 0
+    for i in range(N):
+        p = i + q_offset
+        lo = 0 if window_left < 0 else max(0, p - window_left)
+        hi = M - 1 if window_right < 0 else min(M - 1, p + window_right)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def band_flops(B, H, N, M, D, q_offset=0, window_left=-1, window_right=-1):
+    """4 * D flop per visible pair of the band, over batch rows and heads."""
+    return 4 * D * H * B * band_pairs(N, M, q_offset, window_left, window_right)

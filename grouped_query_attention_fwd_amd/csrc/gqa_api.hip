@@ -179,9 +179,10 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   return GQA_OK;
 }
 
-gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, const uint8_t* mask,
-                         int causal, void* out, int B, int H, int H_kv, int N, int M, int D,
-                         gqa_dtype_t in_dtype, gqa_dtype_t out_dtype, void* stream) {
+gqa_status_t gqa_prefill_band(const void* q, const void* k, const void* v, const uint8_t* mask,
+                              void* out, int B, int H, int H_kv, int N, int M, int D,
+                              int q_offset, int window_left, int window_right,
+                              gqa_dtype_t in_dtype, gqa_dtype_t out_dtype, void* stream) {
   gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, N, M, D, in_dtype, out_dtype);
   if (st != GQA_OK) return st;
   const size_t ein = dtype_size(in_dtype), eout = dtype_size(out_dtype);
@@ -195,11 +196,21 @@ gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, const uint
   a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
   a.B = B; a.H = H; a.H_kv = H_kv; a.N = N; a.M = M; a.D = D;
   a.g = H / H_kv;
-  a.causal = causal != 0;
+  a.q_offset = q_offset;
+  a.wl = window_left < 0 ? -1 : window_left;
+  a.wr = window_right < 0 ? -1 : window_right;
   a.in_bf16 = in_dtype == GQA_BF16;
   a.out_f32 = out_dtype == GQA_F32;
   if (gqa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
+}
+
+gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, const uint8_t* mask,
+                         int causal, void* out, int B, int H, int H_kv, int N, int M, int D,
+                         gqa_dtype_t in_dtype, gqa_dtype_t out_dtype, void* stream) {
+  // causal: the band with no left limit and right edge at the query position
+  return gqa_prefill_band(q, k, v, mask, out, B, H, H_kv, N, M, D, 0, -1, causal ? 0 : -1,
+                          in_dtype, out_dtype, stream);
 }
 
 }  // extern "C"

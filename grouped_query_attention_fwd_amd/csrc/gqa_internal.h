@@ -41,7 +41,10 @@ struct PrefillArgs {
   void* out;
   int B, H, H_kv, N, M, D;
   int g;
-  bool causal;
+  // Band: key j is visible to query i iff
+  //   (wl < 0 || j >= i + q_offset - wl) && (wr < 0 || j <= i + q_offset + wr).
+  // Causal (top-left) is q_offset = 0, wl = -1, wr = 0.
+  int q_offset, wl, wr;
   bool in_bf16;
   bool out_f32;
 };

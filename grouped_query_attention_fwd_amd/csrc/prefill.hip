@@ -5,7 +5,10 @@
 // ("28. Grouped-Query Attention (GQA)", *Reference solution*: repeat-
 // interleave grouping, 1/sqrt(D) scale, [B,N,M] mask broadcast over heads;
 // "Grouped-Query Attention Explained Simply", *Minimal implementation*: the
-// causal self-attention mask, read as key j visible to query i iff j <= i).
+// causal self-attention mask, read as key j visible to query i iff j <= i),
+// generalised to a band: key j is visible to query i iff it lies within
+// window_left keys before and window_right keys after position i + q_offset
+// (either side may be unbounded); causal is the band with right edge 0.
 //
 // Design (flash-style, dense contraction on the matrix cores):
 //   * A workgroup of four waves takes the query heads of one KV group that
@@ -136,7 +139,6 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
 
   const int D = DIRECT ? DP : a.D;
   const int N = a.N, M = a.M;
-  const bool causal = a.causal;
   const int groups_per_kv = a.g / HG;
   // Workgroup -> (unit, position block).  Workgroups are dispatched to the
   // 8 XCDs round-robin (L % 8).  With xcd_major each XCD walks its own units
@@ -154,7 +156,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     unit = L % units;
     pbi = L / units;
   }
-  const int pblk = causal ? (npb - 1 - pbi) : pbi;
+  // the band's upper edge makes later blocks heavier: run them first
+  const int pblk = (a.wr >= 0 && a.wl < 0) ? (npb - 1 - pbi) : pbi;
   const int b = unit / (a.H_kv * groups_per_kv);
   const int rem = unit - b * (a.H_kv * groups_per_kv);
   const int j = rem / groups_per_kv;
@@ -171,12 +174,31 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   const uint8_t* mb = MASKED ? a.mask + (size_t)b * N * M : nullptr;
   const float sl = kLog2e / sqrtf((float)D);
 
+  // Band edges of query position pos, clamped to [0, M]: keys
+  // [key_lo(pos), key_hi(pos)) are visible (before any mask).  Both edges
+  // grow with pos.
+  auto key_lo = [&](int pos) -> int {
+    if (a.wl < 0) return 0;
+    const long long x = (long long)pos + a.q_offset - a.wl;   // no int overflow
+    return (int)(x < 0 ? 0 : (x > M ? M : x));
+  };
+  auto key_hi = [&](int pos) -> int {
+    if (a.wr < 0) return M;
+    const long long x = (long long)pos + a.q_offset + a.wr + 1;
+    return (int)(x < 0 ? 0 : (x > M ? M : x));
+  };
   // key range of the workgroup and of this wave
   const int last_pos = min(N, p0 + PB);          // exclusive
-  const int kend = causal ? min(M, last_pos) : M;
+  const int kbeg = key_lo(p0);
+  const int kend = (p0 < N) ? key_hi(last_pos - 1) : 0;
+  const int t_first = kbeg / C::BN;
   const int ntiles = (kend + C::BN - 1) / C::BN;
   const int w_last = min(N, wp0 + C::RW);        // exclusive
-  const int w_kend = (wp0 >= N) ? 0 : (causal ? min(M, w_last) : M);
+  const int w_kbeg = key_lo(wp0);
+  const int w_kend = (wp0 >= N) ? 0 : key_hi(w_last - 1);
+  // keys every row of this wave sees: [w_full_lo, w_full_hi)
+  const int w_full_lo = (wp0 >= N) ? M : key_lo(w_last - 1);
+  const int w_full_hi = (wp0 >= N) ? 0 : key_hi(wp0);
 
   // Q operands for this wave's rows (zero for rows past N and padded d)
   u32x4 qop[C::QB][C::QCH];
@@ -212,7 +234,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int i = idx / C::BN;
       const int key = k0 + (idx - i * C::BN);
       const int pos = p0 + i;
-      if (pos < N && key < kend && (!causal || key <= pos) && mb[(size_t)pos * M + key]) any = 1;
+      if (pos < N && key < kend && key >= key_lo(pos) && key < key_hi(pos) &&
+          mb[(size_t)pos * M + key])
+        any = 1;
     }
     return __syncthreads_or(any) != 0;
   };
@@ -301,19 +325,19 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     if constexpr (GQA_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
   // Invisible (position, key) pairs of tile t get -inf; only tiles that
-  // cross the diagonal, the end of the keys or a mask pay for this.
+  // cross a band edge, the end of the keys or a mask pay for this.
   auto tile_mask = [&](int t, Scores& sc) {
     const int k0 = t * C::BN;
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const int pos = wp0 + 16 * qb + c16;
-      const int lim = causal ? min(pos + 1, M) : M;  // keys < lim are in range
+      const int lo = key_lo(pos), hi = key_hi(pos);  // keys in [lo, hi) are in range
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + 16 * kb + 4 * qg + r;
-          bool vis = key < lim;
+          bool vis = key >= lo && key < hi;
           if constexpr (MASKED) {
             const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * M + min(key, M - 1)];
             vis = vis && (mbyte != 0) && (pos < N);
@@ -434,7 +458,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   };
   auto tile_needs_mask = [&](int t) {
     const int k0 = t * C::BN;
-    return MASKED || (k0 + C::BN > M) || (causal && k0 + C::BN - 1 > wp0);
+    return MASKED || (k0 + C::BN > M) || k0 < w_full_lo || k0 + C::BN > w_full_hi;
   };
 
   // Double-buffered tile loop: the copy of the next visible tile into the
@@ -450,7 +474,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
         load_stage(tn);
       }
     }
-    if (t * C::BN < w_kend) {
+    if (t * C::BN < w_kend && (t + 1) * C::BN > w_kbeg) {
       Scores sc;
       tile_scores(krd, sc);
       if (tile_needs_mask(t)) tile_mask(t, sc);
@@ -461,7 +485,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     }
     __syncthreads();
   };
-  int t = next_tile(0);
+  int t = next_tile(t_first);
   if (t < ntiles) {
     if constexpr (DIRECT) {
       dma_half(t, k0s, 0);

@@ -173,6 +173,35 @@ gqa_status_t gqa_prefill(const void* q, const void* k, const void* v,
                          gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
                          void* stream);
 
+/*
+ * Banded prefill: gqa_prefill with the visible keys of query i limited to a
+ * band around its position i + q_offset in the key sequence:
+ *
+ *   key j visible  iff  (window_left  < 0 || j >= i + q_offset - window_left)
+ *                   and (window_right < 0 || j <= i + q_offset + window_right)
+ *                   and (mask == NULL || mask[b][i][j] != 0).
+ *
+ * A negative window leaves that side unbounded.  Special cases:
+ *   window_left < 0, window_right = 0, q_offset = 0      causal (= gqa_prefill
+ *                                                          with causal = 1)
+ *   window_left < 0, window_right = 0, q_offset = M - N  bottom-right causal:
+ *       the N queries are the last N positions of the M keys (a prefill
+ *       chunk appended to a cache of M - N earlier keys)
+ *   window_left = W - 1, window_right = 0                 sliding window of W
+ *       keys ending at the query's own position, the local attention that
+ *       "28. Grouped-Query Attention (GQA)" (*Problem*) mentions Mistral
+ *       using alongside GQA.
+ * Key tiles outside every row's band are skipped, so the work is that of the
+ * visible pairs.  Rows that see no key yield NaN.  Same layouts, dtypes,
+ * limits and errors as gqa_prefill; any int q_offset and windows are valid.
+ */
+gqa_status_t gqa_prefill_band(const void* q, const void* k, const void* v,
+                              const uint8_t* mask, void* out,
+                              int B, int H, int H_kv, int N, int M, int D,
+                              int q_offset, int window_left, int window_right,
+                              gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
+                              void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gqa_status_string(gqa_status_t status);
 

@@ -29,6 +29,15 @@ What it computes, and where each step comes from:
   through a per-sequence block table, with one cached length per sequence:
   the result is plain attention over that sequence's first kv_len keys.
 
+* "28. Grouped-Query Attention (GQA)", *Problem*, names sliding-window
+  attention as Mistral's companion to GQA without defining it.
+  `band_visibility` / `gqa_band` read it as a band around each query's
+  position p = i + q_offset in the key sequence: key j is visible iff
+  p - window_left <= j <= p + window_right (a negative window leaves that
+  side open).  Causal is the band with right edge 0 and no left limit;
+  q_offset = M - N places N queries at the end of the M keys (a prefill
+  chunk after a cache).
+
 The page's recipe yields NaN for a query row that sees no key (softmax over an
 empty set: -inf minus -inf); the oracle keeps that NaN on purpose.
 
@@ -49,7 +58,8 @@ import math
 import numpy as np
 
 __all__ = ["validate_shapes", "group_size", "expand_kv", "visibility",
-           "attention_weights", "gqa", "gather_paged", "gqa_paged"]
+           "attention_weights", "gqa", "gather_paged", "gqa_paged",
+           "band_visibility", "gqa_band"]
 
 
 def validate_shapes(q, k, v, mask=None):
@@ -172,3 +182,29 @@ def gqa_paged(q, k_pool, v_pool, block_table, kv_len):
     cache with the length mask."""
     k, v, mask = gather_paged(k_pool, v_pool, block_table, kv_len)
     return gqa(q, k, v, mask)
+
+
+def band_visibility(N, M, q_offset=0, window_left=-1, window_right=-1):
+    """Boolean [N, M]: key j visible to query i iff
+    (window_left < 0 or j >= i + q_offset - window_left) and
+    (window_right < 0 or j <= i + q_offset + window_right)."""
+    i = np.arange(N)[:, None]
+    j = np.arange(M)[None, :]
+    pos = i + q_offset
+    vis = np.ones((N, M), dtype=bool)
+    if window_left >= 0:
+        vis &= j >= pos - window_left
+    if window_right >= 0:
+        vis &= j <= pos + window_right
+    return vis
+
+
+def gqa_band(q, k, v, mask=None, q_offset=0, window_left=-1, window_right=-1):
+    """gqa() with the band of band_visibility ANDed into the mask (the band
+    is the same for every batch row and head)."""
+    B, H, H_kv, N, M, D = validate_shapes(q, k, v, mask)
+    vis = np.broadcast_to(band_visibility(N, M, q_offset, window_left, window_right),
+                          (B, N, M))
+    if mask is not None:
+        vis = vis & np.asarray(mask, dtype=bool)
+    return gqa(q, k, v, np.ascontiguousarray(vis))

@@ -35,7 +35,8 @@ def lib():
 def test_exports_match_header(lib):
     names = declared_functions()
     assert names == ["gqa_decode", "gqa_decode_paged", "gqa_decode_paged_workspace_size",
-                     "gqa_decode_workspace_size", "gqa_prefill", "gqa_status_string"]
+                     "gqa_decode_workspace_size", "gqa_prefill", "gqa_prefill_band",
+                     "gqa_status_string"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", gqa.library_path()],
@@ -62,6 +63,12 @@ def pre(lib, q=Q, k=K, v=V, mask=None, causal=0, out=O, B=2, H=8, H_kv=2, N=7, M
     return lib.gqa_prefill(q, k, v, mask, causal, out, B, H, H_kv, N, M, D, tin, tout, None)
 
 
+def band(lib, q=Q, k=K, v=V, mask=None, out=O, B=2, H=8, H_kv=2, N=7, M=9, D=128,
+         tin=BF16, tout=BF16, q_offset=2, wl=3, wr=0):
+    return lib.gqa_prefill_band(q, k, v, mask, out, B, H, H_kv, N, M, D, q_offset, wl, wr,
+                                tin, tout, None)
+
+
 def paged(lib, q=Q, k=K, v=V, bt=BT, kl=KL, out=O, B=2, H=8, H_kv=2, M=None, D=128,
           tin=BF16, tout=BF16, ws=W, wsb=1 << 30, max_blocks=None, block_size=32,
           num_blocks=64):
@@ -72,7 +79,7 @@ def paged(lib, q=Q, k=K, v=V, bt=BT, kl=KL, out=O, B=2, H=8, H_kv=2, M=None, D=1
                                 num_blocks, D, tin, tout, ws, wsb, None)
 
 
-@pytest.mark.parametrize("fn", [dec, pre, paged])
+@pytest.mark.parametrize("fn", [dec, pre, paged, band])
 def test_rejections_common(lib, fn):
     assert fn(lib, q=None) == NULL
     assert fn(lib, k=None) == NULL
@@ -102,6 +109,8 @@ def test_rejections_common(lib, fn):
 def test_rejections_prefill(lib):
     assert pre(lib, N=0) == SHAPE
     assert pre(lib, mask=O) == ALIAS
+    assert band(lib, N=0) == SHAPE
+    assert band(lib, mask=O) == ALIAS
 
 
 def test_rejections_decode_workspace(lib):

@@ -54,3 +54,13 @@ def test_visible_pairs_brute_force():
 def test_causal_prefill_flops():
     # B4 H32 N=M=4096 D128 causal: 4*D*B*H*N(N+1)/2
     assert accounting.prefill_flops(4, 32, 4096, 4096, 128, causal=True) == 549890031616
+
+
+def test_band_pairs_brute_force():
+    for N, M, qo, wl, wr in [(5, 5, 0, -1, 0), (6, 9, 3, 2, 0), (9, 4, -2, 1, 1), (7, 7, 0, -1, -1),
+                             (4, 10, 6, -1, 0), (8, 8, 0, 3, -1), (5, 5, -9, -1, 0)]:
+        brute = sum(1 for i in range(N) for j in range(M)
+                    if (wl < 0 or j >= i + qo - wl) and (wr < 0 or j <= i + qo + wr))
+        assert accounting.band_pairs(N, M, qo, wl, wr) == brute
+    # causal at offset 0 is the causal count
+    assert accounting.band_pairs(33, 17, 0, -1, 0) == accounting.visible_pairs(33, 17, causal=True)

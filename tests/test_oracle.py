@@ -410,6 +410,52 @@ def pin_paged_block_permutation(orc):
     np.testing.assert_allclose(base, shared, rtol=1e-12, atol=1e-13)
 
 
+def pin_band_causal_is_causal(orc):
+    """The band with no left limit and right edge 0 at offset 0 is the causal
+    rule, bit for bit; with both sides open it is no mask at all."""
+    q, k, v = rand_qkv(70, 2, 4, 2, 7, 9, 4)
+    assert np.array_equal(orc.gqa_band(q, k, v, None, 0, -1, 0), orc.gqa(q, k, v, causal=True))
+    assert np.array_equal(orc.gqa_band(q, k, v, None, 3, -1, -1), orc.gqa(q, k, v))
+
+
+def pin_band_bottom_right_is_a_chunk(orc):
+    """N queries placed at the end of M keys (offset M - N, causal) are the
+    last N rows of causal self-attention over all M positions."""
+    B, H, H_kv, M, N, D = 2, 6, 3, 11, 4, 8
+    r = rng(71)
+    q_full = r.standard_normal((B, H, M, D))
+    k = r.standard_normal((B, H_kv, M, D))
+    v = r.standard_normal((B, H_kv, M, D))
+    full = orc.gqa(q_full, k, v, causal=True)
+    chunk = orc.gqa_band(q_full[:, :, M - N:], k, v, None, M - N, -1, 0)
+    np.testing.assert_allclose(chunk, full[:, :, M - N:], rtol=1e-13, atol=1e-14)
+    # a single query at the end is plain decode over every key
+    dec = orc.gqa_band(q_full[:, :, M - 1:], k, v, None, M - 1, -1, 0)
+    np.testing.assert_allclose(dec, orc.gqa(q_full[:, :, M - 1:], k, v), rtol=1e-13, atol=1e-14)
+
+
+def pin_band_brute_force(orc):
+    """Sliding windows and two-sided bands against pure-Python loops, with a
+    mask on top and offsets that leave some rows empty (NaN)."""
+    B, H, H_kv, N, M, D = 2, 4, 2, 6, 9, 4
+    q, k, v = rand_qkv(72, B, H, H_kv, N, M, D)
+    extra = rng(73).random((B, N, M)) < 0.8
+    for q_off, wl, wr in [(0, 2, 0), (3, 1, 1), (-2, 0, 3), (5, -1, 2), (0, 3, -1), (-8, -1, 0)]:
+        mask = [[[bool(extra[b][i][j]) and (wl < 0 or j >= i + q_off - wl)
+                  and (wr < 0 or j <= i + q_off + wr)
+                  for j in range(M)] for i in range(N)] for b in range(B)]
+        got = orc.gqa_band(q, k, v, extra, q_off, wl, wr)
+        ref = brute_force(q, k, v, mask)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_band_wide_window_is_causal(orc):
+    """A window at least as long as the keys changes nothing."""
+    q, k, v = rand_qkv(74, 1, 4, 1, 8, 8, 4)
+    np.testing.assert_allclose(orc.gqa_band(q, k, v, None, 0, 8, 0),
+                               orc.gqa(q, k, v, causal=True), rtol=0, atol=0)
+
+
 PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
         pin_mha_equals_per_head, pin_mqa_brute_force, pin_single_key,
         pin_two_keys_closed_form, pin_scale_exact, pin_zero_keys_give_mean,
@@ -417,7 +463,8 @@ PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
         pin_masked_keys_contribute_nothing, pin_causal_properties,
         pin_key_permutation, pin_empty_row_is_nan, pin_rejects_bad_group,
         pin_paged_brute_force, pin_paged_identity_table, pin_paged_length_is_truncation,
-        pin_paged_block_permutation]
+        pin_paged_block_permutation, pin_band_causal_is_causal,
+        pin_band_bottom_right_is_a_chunk, pin_band_brute_force, pin_band_wide_window_is_causal]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -465,6 +512,10 @@ MUTANTS = {
     "paged_block_index": (r"table\[b, t // bs\]", "table[b, t % max_blocks]"),
     "paged_length_inclusive": (r"for t in range\(n\):", "for t in range(min(n + 1, M)):"),
     "paged_v_from_k": (r"v\[b, :, t, :\] = v_pool", "v[b, :, t, :] = k_pool"),
+    "band_left_strict": (r"vis &= j >= pos - window_left", "vis &= j > pos - window_left"),
+    "band_right_strict": (r"vis &= j <= pos \+ window_right", "vis &= j < pos + window_right"),
+    "band_offset_sign": (r"pos = i \+ q_offset", "pos = i - q_offset"),
+    "band_mask_dropped": (r"vis = vis & np\.asarray\(mask, dtype=bool\)", "vis = vis"),
     "paged_head_ignored": (r"k\[b, :, t, :\] = k_pool\[blk, :,", "k[b, :, t, :] = k_pool[blk, :1,"),
 }
 

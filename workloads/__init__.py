@@ -45,10 +45,21 @@ class Workload:
     dtype: str          # "fp32" or "bf16"
     causal: bool = False
     padded: bool = False  # padding mask j < len_b, len_b ~ U{1..M}
+    # band around position i + q_offset: window_left keys before, window_right
+    # after (-1 = open); used by the banded prefill workloads
+    q_offset: int = 0
+    window_left: int = -1
+    window_right: int = -1
+
+    @property
+    def band(self):
+        if self.q_offset == 0 and self.window_left < 0 and self.window_right < 0:
+            return None
+        return (self.q_offset, self.window_left, self.window_right)
 
     @property
     def kind(self) -> str:
-        return "decode" if self.N == 1 and not self.causal else "prefill"
+        return "decode" if self.N == 1 and not self.causal and self.band is None else "prefill"
 
     @property
     def torch_dtype(self):
@@ -63,6 +74,14 @@ WORKLOADS = [
              causal=True),
     Workload("prefill_padded_d24", 5, 4, 32, 4, 512, 512, 24, "fp32",
              padded=True),
+    # sliding window of 4096 keys (Mistral-style local attention) over a
+    # 16K-token self-attention prefill
+    Workload("prefill_window4096_n16384", 8, 1, 32, 8, 16384, 16384, 128, "bf16",
+             window_left=4095, window_right=0),
+    # a 512-token prefill chunk appended to 3584 cached keys: bottom-right
+    # causal over M = 4096
+    Workload("prefill_chunk512_m4096", 9, 16, 32, 8, 512, 4096, 128, "bf16",
+             q_offset=3584, window_right=0),
 ]
 
 
