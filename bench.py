@@ -433,6 +433,25 @@ def main():
             del info
             torch.cuda.empty_cache()
 
+    # group-size sweep: the same decode step with 64 query heads and
+    # g = 1 ... 64; enough rotating copies that each point streams from HBM
+    sweep = []
+    if not args.skip_secondary and not args.only:
+        import workloads
+        from grouped_query_attention_fwd_amd import accounting
+        for w in workloads.GROUP_SWEEP:
+            kv = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, 2)
+            copies_g = max(1, -(-(640 << 20) // kv))
+            log(f"[bench] group sweep {w.name} ({copies_g} copies)")
+            info = setup(w.name, torch, copies=copies_g)
+            timing = time_workload(info, max(10, args.steps // 2), args.warmup, torch)
+            r = result_for(info, timing)
+            sweep.append({"g": w.H // w.H_kv, "H_kv": w.H_kv, "value": r["value"],
+                          "unit": r["unit"], "launch_us": r["launch_us"]["avg"],
+                          "frac": r["roofline"]["frac"], "kv_bytes": kv})
+            del info
+            torch.cuda.empty_cache()
+
     p = results[primary]
     line = {
         "metric": METRIC,
@@ -462,6 +481,9 @@ def main():
         line["secondary"] = [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step",
                                                 "launch_us", "graph_us_per_launch", "roofline")}
                              for r in sec]
+    if sweep:
+        line["group_sweep"] = {"workload": "decode B16 H64 M4096 D128 bf16, H_kv = 64 / g",
+                               "points": sweep}
     print(json.dumps(line), flush=True)
     return 0
 

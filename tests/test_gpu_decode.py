@@ -138,3 +138,16 @@ def test_decode_llama70b_full_sampled():
         ref = oracle_out(q[b:b + 1], k[b:b + 1], v[b:b + 1])
         mx, rr = compare(out[b:b + 1], ref, TOL[torch.bfloat16], f"{w.name} b={b}")
         say(f"  b={b} max abs err {mx:.3e} rel rms {rr:.3e}")
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.GROUP_SWEEP])
+def test_decode_group_sweep_sampled(name):
+    """The group-size sweep (64 query heads, g = 1 ... 64) at full size in
+    the benchmarked launch configuration; two batch rows against the oracle."""
+    w = workloads.by_name(name)
+    q, k, v, _, _ = workloads.make_inputs(w)
+    say(f"decode group sweep {name}")
+    out = gqa.decode(*to_dev(q, k, v)).cpu()
+    for b in (0, w.B - 1):
+        ref = oracle_out(q[b:b + 1], k[b:b + 1], v[b:b + 1])
+        compare(out[b:b + 1], ref, TOL[torch.bfloat16], f"{name} b={b}")

@@ -27,7 +27,7 @@ import dataclasses
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "make_inputs", "random_case",
+__all__ = ["Workload", "WORKLOADS", "GROUP_SWEEP", "by_name", "make_inputs", "random_case",
            "PagedWorkload", "PAGED_WORKLOADS", "paged_by_name", "make_paged_inputs",
            "random_paged_case"]
 
@@ -85,8 +85,16 @@ WORKLOADS = [
 ]
 
 
+# Group-size sweep: decode with 64 query heads and g = H / H_kv from 1 (MHA,
+# 64 KV heads) to 64 (MQA, one KV head), B16, M 4096, D 128, bf16.
+GROUP_SWEEP = [
+    Workload(f"decode_h64_g{g}_m4096", 100 + g, 16, 64, 64 // g, 1, 4096, 128, "bf16")
+    for g in (1, 2, 4, 8, 16, 32, 64)
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + GROUP_SWEEP:
         if w.name == name:
             return w
     raise KeyError(name)
