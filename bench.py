@@ -9,8 +9,9 @@ N = M = 4096, D 128; TFLOP/s over the visible pairs) and the paged decode of
 the Mistral-shaped batch (blocks of 16 keys scattered over a pool; mixed
 lengths, and all lengths 4096; GB/s over each sequence's own keys) and two
 banded prefills (a 4096-key sliding window over N = M = 16384, and a
-512-query chunk after 3584 cached keys, bottom-right causal), which appear
-under "secondary".
+512-query chunk after 3584 cached keys, bottom-right causal) and the
+headline decode and causal prefill with fp16 inputs, which appear under
+"secondary".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-secondary]
                     [--no-cpu-baseline] [--only WORKLOAD]
@@ -79,7 +80,7 @@ def setup_paged(name, torch, copies=1):
     w = workloads.paged_by_name(name)
     cpu = workloads.make_paged_inputs(w)
     sets = [[t.cuda() if c == 0 else t.cuda().clone() for t in cpu] for c in range(copies)]
-    elt = 2 if w.dtype == "bf16" else 4
+    elt = 4 if w.dtype == "fp32" else 2
     info = {"w": w, "kind": "decode_paged", "cpu": cpu, "sets": sets,
             "units": accounting.paged_decode_bytes(cpu[4].tolist(), w.H_kv, w.D, elt)}
     return info
@@ -98,7 +99,7 @@ def setup(name, torch, copies=1):
             sets.append([t.cuda() if t is not None else None for t in (q, k, v, mask)])
         else:   # distinct buffers with the same contents
             sets.append([t.cuda().clone() if t is not None else None for t in (q, k, v, mask)])
-    elt = 2 if w.dtype == "bf16" else 4
+    elt = 4 if w.dtype == "fp32" else 2
     info = {"w": w, "kind": w.kind, "cpu": (q, k, v, mask, causal), "sets": sets}
     if w.kind == "decode":
         info["units"] = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, elt)
@@ -244,7 +245,7 @@ def result_for(info, timing):
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         unit = "GB/s"
     else:
-        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        peak = FP32_PEAK_TFLOPS if w.dtype == "fp32" else BF16_PEAK_TFLOPS  # fp16 = bf16 rate
         achieved = info["units"] / avg_s / 1e12
         value = info["units"] / whole_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -412,8 +413,9 @@ def main():
     if not args.skip_secondary and not args.only:
         names += ["decode_llama70b_m32768", "prefill_causal_n4096",
                   "decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full",
-                  "prefill_window4096_n16384", "prefill_chunk512_m4096"]
-    copies = {"decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1,
+                  "prefill_window4096_n16384", "prefill_chunk512_m4096",
+                  "decode_mistral7b_m4096_fp16", "prefill_causal_n4096_fp16"]
+    copies = {"decode_mistral7b_m4096_fp16": 4, "decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1,
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}
     primary_info = None
@@ -464,7 +466,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if primary_info["w"].dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp16": "f16", "fp32": "f32"}[primary_info["w"].dtype],
         "data": "synthetic: seeded i.i.d. N(0,1) q/k/v at the workload's shapes",
         "config": p["config"],
         "roofline": p["roofline"],

@@ -41,7 +41,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
 _lib = None
 
-GQA_F32, GQA_BF16 = 0, 1
+GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
 _STATUS_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9}
 
 
@@ -117,7 +117,9 @@ def _dtype_code(t):
         return GQA_F32
     if t == torch.bfloat16:
         return GQA_BF16
-    raise ValueError(f"unsupported dtype {t} (float32 or bfloat16)")
+    if t == torch.float16:
+        return GQA_F16
+    raise ValueError(f"unsupported dtype {t} (float32, bfloat16 or float16)")
 
 
 def _check_tensors(q, k, v, mask, same_batch=True):

@@ -50,21 +50,21 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #define GQA_DECODE_PAGED_TARGET_WGS 256
 #endif
 
-template <bool BF16, int DP>
+template <bool H16, int DP>
 struct DecCfg {
-  static constexpr int ELT = BF16 ? 2 : 4;
+  static constexpr int ELT = H16 ? 2 : 4;
   // keys per wave chunk (bounded by LDS and by the registers of the loads)
-  static constexpr int KC = BF16 ? (DP <= 64 ? 64 : 32) : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));
+  static constexpr int KC = H16 ? (DP <= 64 ? 64 : 32) : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));
   static constexpr int NKB = KC / 16;                 // 16-key MFMA blocks per chunk
   static constexpr int NDB = DP / 16;                 // 16-wide d blocks of O
-  static constexpr int QCH = BF16 ? DP / 32 : DP / 16;  // 16-byte Q/K chunks per lane per key
+  static constexpr int QCH = H16 ? DP / 32 : DP / 16;  // 16-byte Q/K chunks per lane per key
   static constexpr int CPR = DP * ELT / 16;           // 16-byte chunks per row
-  static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16;  // LDS row stride (fp32 rows padded)
+  static constexpr int ROWB = H16 ? DP * 2 : DP * 4 + 16;  // LDS row stride (fp32 rows padded)
   static constexpr int VBYTES = KC * ROWB;            // LDS bytes of one wave's V chunk
   static constexpr int VLOADS = KC * CPR / 64;        // 16-byte V loads per lane per chunk
   // the rows of one V load instruction lie in one aligned group of 16 keys
   static_assert(KC % 16 == 0 && 64 % CPR == 0 && 64 / CPR <= 16, "V load rows span a group");
-  static constexpr int SPR = DP / 16;                 // 32-byte segments per bf16 row
+  static constexpr int SPR = DP / 16;                 // 32-byte segments per 16-bit row
   static constexpr int SWZ = (SPR < 8 ? SPR : 8) - 1;
   // Registers of one chunk's loads; when two chunks fit, the next chunk is
   // loaded while the current one is computed.
@@ -76,31 +76,34 @@ struct DecCfg {
 };
 
 // Byte offset of 16-byte chunk `chunk` of LDS row `row` of a V chunk.
-template <bool BF16, int DP>
+template <bool H16, int DP>
 __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
-  using C = DecCfg<BF16, DP>;
-  if constexpr (BF16) {
+  using C = DecCfg<H16, DP>;
+  if constexpr (H16) {
     return row * C::ROWB + ((chunk ^ (2 * (row & C::SWZ))) << 4);
   } else {
     return row * C::ROWB + (chunk << 4);
   }
 }
 
-template <bool OUTF32>
+// Output element idx: fp32, or the 16-bit input type ET.
+template <int ET, bool OUTF32>
 __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
   if constexpr (OUTF32) {
     reinterpret_cast<float*>(out)[idx] = x;
   } else {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16(x);
+    static_assert(ET != kF32, "fp32 inputs have fp32 outputs");
+    reinterpret_cast<uint16_t*>(out)[idx] = cvt16<ET>(x);
   }
 }
 
 // EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is
 // given.  PAGED: K/V rows are found through a block table and each sequence
 // has its own length.
-template <bool BF16, int DP, bool EXACT, bool MASKED, bool PAGED, bool OUTF32>
+template <int ET, int DP, bool EXACT, bool MASKED, bool PAGED, bool OUTF32>
 __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs a) {
-  using C = DecCfg<BF16, DP>;
+  constexpr bool H16 = ET != kF32;  // 16-bit elements: bf16 or fp16
+  using C = DecCfg<H16, DP>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
   lds_char* smem = (lds_char*)smem_raw;
 
@@ -167,7 +170,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
                      ((size_t)b * a.H + h0 + (hv ? c16 : 0)) * (size_t)D * C::ELT;
 #pragma unroll
     for (int u = 0; u < C::QCH; ++u) {
-      const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+      const int d0 = H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
       const bool dv = EXACT || d0 < D;
       qop[u] = sel16(hv && dv, ld16(qp + (size_t)(dv ? d0 : 0) * C::ELT));
     }
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       const char* krow = kp + goff[kb] + (size_t)(key - g16[kb]) * D * C::ELT;
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
-        const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+        const int d0 = H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
         if constexpr (EXACT) {
           ch.k[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
         } else {
@@ -255,8 +258,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
-        if constexpr (BF16) {
-          c = mfma_bf16(__builtin_bit_cast(bf16x8, kop[kb][u]), __builtin_bit_cast(bf16x8, qop[u]), c);
+        if constexpr (H16) {
+          c = mma16<ET>(kop[kb][u], qop[u], c);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -271,7 +274,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       const int piece = it * 64 + lane;
       const int row = piece / C::CPR;
       const int chunk = piece - row * C::CPR;
-      lds_st16(vl, v_off<BF16, DP>(row, chunk), vreg[it]);
+      lds_st16(vl, v_off<H16, DP>(row, chunk), vreg[it]);
     }
     // ---- visibility + online softmax --------------------------------------
     float mloc = kNegInf;
@@ -312,21 +315,21 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- O^T += V^T P^T ---------------------------------------------------
-    if constexpr (BF16) {
+    if constexpr (H16) {
 #pragma unroll
       for (int c = 0; c < C::NKB / 2; ++c) {
         float pp[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
                        p[2 * c + 1][0], p[2 * c + 1][1], p[2 * c + 1][2], p[2 * c + 1][3]};
-        const bf16x8 bop = to_bf16x8(pp);
+        const u32x4 bop = pack16x8<ET>(pp);
         const int row_a = 32 * c + 4 * qg + (c16 >> 2);
         const int row_b = row_a + 16;
         const int within = (c16 & 1) << 3;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           const int chunk = 2 * db + ((c16 & 3) >> 1);
-          const i16x4 ta = lds_ld_tr16(vl, v_off<BF16, DP>(row_a, chunk) + within);
-          const i16x4 tb = lds_ld_tr16(vl, v_off<BF16, DP>(row_b, chunk) + within);
-          acc[db] = mfma_bf16(concat_bf16(ta, tb), bop, acc[db]);
+          const i16x4 ta = lds_ld_tr16(vl, v_off<H16, DP>(row_a, chunk) + within);
+          const i16x4 tb = lds_ld_tr16(vl, v_off<H16, DP>(row_b, chunk) + within);
+          acc[db] = mma16<ET>(concat16(ta, tb), bop, acc[db]);
         }
       }
     } else {
@@ -391,7 +394,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       A = fmaf(cacc[(ww * 16 + hh) * DP + d], f, A);
     }
     if (single) {
-      store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+      store_out<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
     } else {
       float* ph = part + (size_t)hh * (D + 2);
       if (d == 0) {
@@ -410,7 +413,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
 constexpr int kMergeThreads = 128;
 // MAXS > 0: at most MAXS splits; every partial is loaded up front (indexes
 // clamped to the last split) so the loads overlap.  MAXS == 0: any count.
-template <bool OUTF32, int MAXS>
+template <int ET, bool OUTF32, int MAXS>
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a) {
   const int unit = blockIdx.x;
   const int per_b = a.H_kv * a.head_chunks;
@@ -462,49 +465,49 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
       A = fmaf(p[2 + d], f, A);
     }
   }
-  store_out<OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+  store_out<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
 }
 
-template <bool BF16, int DP, bool EXACT, bool OUTF32>
+template <int ET, int DP, bool EXACT, bool OUTF32>
 hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * a.head_chunks;
   const dim3 grid(units, a.splits);
   if (a.block_table) {  // the paged form takes no mask
-    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else if (a.mask) {
-    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, true, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, true, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<BF16, DP, EXACT, false, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int per_unit = (a.head_chunk * a.D + kMergeThreads - 1) / kMergeThreads;
   const dim3 mgrid(units, per_unit);
   if (a.splits <= 2) {
-    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 2>), mgrid, dim3(kMergeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 2>), mgrid, dim3(kMergeThreads), 0, stream, a);
   } else if (a.splits <= 8) {
-    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 8>), mgrid, dim3(kMergeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 8>), mgrid, dim3(kMergeThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_merge_kernel<OUTF32, 0>), mgrid, dim3(kMergeThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 0>), mgrid, dim3(kMergeThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <bool BF16, int DP, bool OUTF32>
+template <int ET, int DP, bool OUTF32>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
-  return a.D == DP ? launch_dp<BF16, DP, true, OUTF32>(a, stream)
-                   : launch_dp<BF16, DP, false, OUTF32>(a, stream);
+  return a.D == DP ? launch_dp<ET, DP, true, OUTF32>(a, stream)
+                   : launch_dp<ET, DP, false, OUTF32>(a, stream);
 }
 
-template <bool BF16, bool OUTF32>
+template <int ET, bool OUTF32>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if constexpr (!BF16) {
-    if (a.D <= 16) return launch_d<BF16, 16, OUTF32>(a, stream);
+  if constexpr (ET == kF32) {
+    if (a.D <= 16) return launch_d<ET, 16, OUTF32>(a, stream);
   }
-  if (a.D <= 32) return launch_d<BF16, 32, OUTF32>(a, stream);
-  if (a.D <= 64) return launch_d<BF16, 64, OUTF32>(a, stream);
-  if (a.D <= 128) return launch_d<BF16, 128, OUTF32>(a, stream);
-  return launch_d<BF16, 256, OUTF32>(a, stream);
+  if (a.D <= 32) return launch_d<ET, 32, OUTF32>(a, stream);
+  if (a.D <= 64) return launch_d<ET, 64, OUTF32>(a, stream);
+  if (a.D <= 128) return launch_d<ET, 128, OUTF32>(a, stream);
+  return launch_d<ET, 256, OUTF32>(a, stream);
 }
 
 }  // namespace
@@ -541,10 +544,14 @@ DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.in_bf16) {
-    return a.out_f32 ? launch_t<true, true>(a, stream) : launch_t<true, false>(a, stream);
+  switch (a.in_type) {
+    case kBF16:
+      return a.out_f32 ? launch_t<kBF16, true>(a, stream) : launch_t<kBF16, false>(a, stream);
+    case kF16:
+      return a.out_f32 ? launch_t<kF16, true>(a, stream) : launch_t<kF16, false>(a, stream);
+    default:
+      return launch_t<kF32, true>(a, stream);
   }
-  return launch_t<false, true>(a, stream);
 }
 
 }  // namespace gqa

@@ -12,9 +12,9 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t dtype_size(gqa_dtype_t t) { return t == GQA_BF16 ? 2 : 4; }
+size_t dtype_size(gqa_dtype_t t) { return t == GQA_F32 ? 4 : 2; }
 
-bool dtype_ok(gqa_dtype_t t) { return t == GQA_F32 || t == GQA_BF16; }
+bool dtype_ok(gqa_dtype_t t) { return t == GQA_F32 || t == GQA_BF16 || t == GQA_F16; }
 
 // [lo, lo + n) overlaps [p, p + m)?
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -110,7 +110,7 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
   a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
-  a.in_bf16 = in_dtype == GQA_BF16;
+  a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
@@ -172,7 +172,7 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
-  a.in_bf16 = in_dtype == GQA_BF16;
+  a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
@@ -199,7 +199,7 @@ gqa_status_t gqa_prefill_band(const void* q, const void* k, const void* v, const
   a.q_offset = q_offset;
   a.wl = window_left < 0 ? -1 : window_left;
   a.wr = window_right < 0 ? -1 : window_right;
-  a.in_bf16 = in_dtype == GQA_BF16;
+  a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (gqa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;

@@ -6,6 +6,7 @@
 //     C[4*(l/16)+r][l%16].
 //   v_mfma_f32_16x16x4f32: lane l holds A[l%16][l/16] and B[l/16][l%16];
 //     the result uses the same C layout.
+//   v_mfma_f32_16x16x32_f16: the same layout as the bf16 form.
 // Both attention products are formed transposed, S^T = K Q^T and
 // O^T = V^T P^T, so a lane always owns one query (or one query head) in the
 // column index l%16 and four consecutive keys (or d) in its registers.
@@ -24,6 +25,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) char lds_char;
+
+// Element types of q, k and v (values of the C ABI's gqa_dtype_t).
+enum : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -57,19 +61,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
-// Eight fp32 values -> one bf16x8 MFMA operand (round to nearest even).
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
-  u32x4 w;
-  w[0] = pack_bf16x2(x[0], x[1]);
-  w[1] = pack_bf16x2(x[2], x[3]);
-  w[2] = pack_bf16x2(x[4], x[5]);
-  w[3] = pack_bf16x2(x[6], x[7]);
-  return __builtin_bit_cast(bf16x8, w);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// ---- 16-bit element types (ET = kBF16 or kF16) -------------------------
+// 16x16x32 matrix-core product on operands held as raw 16-byte words.
+template <int ET>
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+  static_assert(ET == kBF16 || ET == kF16, "16-bit element types only");
+  if constexpr (ET == kBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, z);
+// Two fp32 -> one packed pair of ET (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32:
+// round to nearest, ties to even).  `lo` lands in the low half.
+template <int ET>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (ET == kBF16) return pack_bf16x2(lo, hi);
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+template <int ET>
+__device__ __forceinline__ uint16_t cvt16(float f) {
+  return (uint16_t)(pack16<ET>(f, 0.f) & 0xffffu);
+}
+
+// Eight fp32 values -> one 16-byte MFMA operand of ET.
+template <int ET>
+__device__ __forceinline__ u32x4 pack16x8(const float* x) {
+  u32x4 w;
+  w[0] = pack16<ET>(x[0], x[1]);
+  w[1] = pack16<ET>(x[2], x[3]);
+  w[2] = pack16<ET>(x[4], x[5]);
+  w[3] = pack16<ET>(x[6], x[7]);
+  return w;
 }
 
 // 16-byte global load (caller guarantees 16-byte alignment).
@@ -113,10 +144,11 @@ __device__ __forceinline__ i16x4 lds_ld_tr16(lds_char* base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
 }
 
-__device__ __forceinline__ bf16x8 concat_bf16(i16x4 a, i16x4 b) {
+// Two transposed reads -> one 16-byte operand (any 16-bit element type).
+__device__ __forceinline__ u32x4 concat16(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, c);
+  return __builtin_bit_cast(u32x4, c);
 }
 
 // Cross-lane reductions inside a wave.

@@ -29,7 +29,7 @@ struct DecodeArgs {
   int xcd_group;        // 1: the head chunks of one (b, KV head) share an XCD
   int splits;           // key-range splits per unit
   int keys_per_split;   // multiple of 256
-  bool in_bf16;
+  int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };
 
@@ -45,7 +45,7 @@ struct PrefillArgs {
   //   (wl < 0 || j >= i + q_offset - wl) && (wr < 0 || j <= i + q_offset + wr).
   // Causal (top-left) is q_offset = 0, wl = -1, wr = 0.
   int q_offset, wl, wr;
-  bool in_bf16;
+  int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };
 

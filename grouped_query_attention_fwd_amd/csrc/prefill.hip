@@ -64,60 +64,61 @@ constexpr int kThreads = 64 * kWaves;
 // Rescale threshold of the online softmax, in log2 units (weights <= 2^8).
 constexpr float kLazy = 8.f;
 
-template <bool BF16, int DP>
+template <bool H16, int DP>
 struct PreCfg {
-  static constexpr int ELT = BF16 ? 2 : 4;
+  static constexpr int ELT = H16 ? 2 : 4;
 #ifndef GQA_PREFILL_QB
 #define GQA_PREFILL_QB 2
 #endif
-  static constexpr int QB = (BF16 && DP <= 128) ? GQA_PREFILL_QB : 1;  // 16-row query blocks per wave
+  static constexpr int QB = (H16 && DP <= 128) ? GQA_PREFILL_QB : 1;  // 16-row query blocks per wave
   static constexpr int RW = 16 * QB;                       // query rows per wave
 #ifndef GQA_PREFILL_BN
 #define GQA_PREFILL_BN 64
 #endif
-  static constexpr int BN = BF16 ? GQA_PREFILL_BN
+  static constexpr int BN = H16 ? GQA_PREFILL_BN
                                  : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
   static constexpr int NKB = BN / 16;
   static constexpr int NDB = DP / 16;
-  static constexpr int QCH = BF16 ? DP / 32 : DP / 16;     // 16-byte operand chunks per lane
+  static constexpr int QCH = H16 ? DP / 32 : DP / 16;     // 16-byte operand chunks per lane
   static constexpr int CPR = DP * ELT / 16;                // 16-byte chunks per row
-  static constexpr int ROWB = BF16 ? DP * 2 : DP * 4 + 16; // LDS row stride
+  static constexpr int ROWB = H16 ? DP * 2 : DP * 4 + 16; // LDS row stride
   static constexpr int TILE = BN * ROWB;                   // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;                   // K + V
   static constexpr int PIECES = 2 * BN * CPR;              // 16-byte pieces per stage
   static constexpr int PPT = PIECES / kThreads;            // pieces per thread
   static constexpr int KSWZ = (CPR < 16 ? CPR : 16) - 1;   // K row swizzle mask
-  static constexpr int SPR = DP / 16;                      // 32-byte segments per bf16 row
+  static constexpr int SPR = DP / 16;                      // 32-byte segments per 16-bit row
   static constexpr int VSWZ = (SPR < 8 ? SPR : 8) - 1;     // V row swizzle mask
   // direct copies: one wave instruction fills 1 KB = RPI rows of a tile
-  static constexpr int RPI = BF16 ? 1024 / ROWB : 1;
-  static constexpr int DMA_INSTS = BF16 ? BN / RPI : 0;                  // per K or V tile
+  static constexpr int RPI = H16 ? 1024 / ROWB : 1;
+  static constexpr int DMA_INSTS = H16 ? BN / RPI : 0;                  // per K or V tile
   static constexpr int DMA_PER_TILE = (DMA_INSTS + kWaves - 1) / kWaves;  // per wave
   static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
-  static_assert(!BF16 || (BN % RPI == 0), "direct copy must cover whole rows");
+  static_assert(!H16 || (BN % RPI == 0), "direct copy must cover whole rows");
 };
 
-template <bool BF16, int DP>
+template <bool H16, int DP>
 __device__ __forceinline__ uint32_t k_off(int row, int chunk) {
-  using C = PreCfg<BF16, DP>;
-  if constexpr (BF16) return row * C::ROWB + ((chunk ^ (row & C::KSWZ)) << 4);
+  using C = PreCfg<H16, DP>;
+  if constexpr (H16) return row * C::ROWB + ((chunk ^ (row & C::KSWZ)) << 4);
   else return row * C::ROWB + (chunk << 4);
 }
 
-template <bool BF16, int DP>
+template <bool H16, int DP>
 __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
-  using C = PreCfg<BF16, DP>;
-  if constexpr (BF16) return row * C::ROWB + ((chunk ^ (2 * (row & C::VSWZ))) << 4);
+  using C = PreCfg<H16, DP>;
+  if constexpr (H16) return row * C::ROWB + ((chunk ^ (2 * (row & C::VSWZ))) << 4);
   else return row * C::ROWB + (chunk << 4);
 }
 
-// DIRECT: bf16 with D == DP, tiles copied straight into LDS.
-// MASKED: a [B,N,M] mask is given.
-template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
+// ET: element type of q, k, v.  DIRECT: 16-bit elements with D == DP, tiles
+// copied straight into LDS.  MASKED: a [B,N,M] mask is given.
+template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32>
 __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillArgs a, int HG, int units, int npb,
                                                                      int xcd_major) {
-  using C = PreCfg<BF16, DP>;
-  static_assert(!DIRECT || BF16, "direct copies are for bf16 tiles");
+  constexpr bool H16 = ET != kF32;  // 16-bit elements: bf16 or fp16
+  using C = PreCfg<H16, DP>;
+  static_assert(!DIRECT || H16, "direct copies are for 16-bit tiles");
   // Two stages as two distinct LDS objects: with the loop unrolled by two
   // every access names its stage statically, so the compiler can tell that
   // reads of one stage never alias the copy in flight into the other (it
@@ -210,7 +211,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
                      (((size_t)b * a.H + h) * N + (pv ? pos : 0)) * (size_t)D * C::ELT;
 #pragma unroll
     for (int u = 0; u < C::QCH; ++u) {
-      const int d0 = BF16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
+      const int d0 = H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
       const bool dv = DIRECT || d0 < D;
       qop[qb][u] = sel16(pv && dv, ld16(qp + (size_t)(dv ? d0 : 0) * C::ELT));
     }
@@ -289,8 +290,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int rr = piece - which * (C::BN * C::CPR);
       const int row = rr / C::CPR;
       const int chunk = rr - row * C::CPR;
-      if (which) lds_st16(vt, v_off<BF16, DP>(row, chunk), stage[it]);
-      else lds_st16(kt, k_off<BF16, DP>(row, chunk), stage[it]);
+      if (which) lds_st16(vt, v_off<H16, DP>(row, chunk), stage[it]);
+      else lds_st16(kt, k_off<H16, DP>(row, chunk), stage[it]);
     }
   };
 
@@ -308,12 +309,11 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
-        const u32x4 kop = lds_ld16(kbuf_lds, k_off<BF16, DP>(16 * kb + c16, 4 * u + qg));
+        const u32x4 kop = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * u + qg));
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
-          if constexpr (BF16) {
-            sc[qb][kb] = mfma_bf16(__builtin_bit_cast(bf16x8, kop),
-                                   __builtin_bit_cast(bf16x8, qop[qb][u]), sc[qb][kb]);
+          if constexpr (H16) {
+            sc[qb][kb] = mma16<ET>(kop, qop[qb][u], sc[qb][kb]);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -384,10 +384,10 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     float msl[C::QB];
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) msl[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb] * sl;
-    if constexpr (BF16) {
+    if constexpr (H16) {
 #pragma unroll
       for (int c = 0; c < C::NKB / 2; ++c) {
-        bf16x8 bop[C::QB];
+        u32x4 bop[C::QB];
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
           float pp[8];
@@ -396,12 +396,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
             pp[e] = exp2_hw(fmaf(sc[qb][2 * c + (e >> 2)][e & 3], sl, -msl[qb]));
             l_run[qb] += pp[e];
           }
-          u32x4 wv;
-          wv[0] = pack_bf16x2(pp[0], pp[1]);
-          wv[1] = pack_bf16x2(pp[2], pp[3]);
-          wv[2] = pack_bf16x2(pp[4], pp[5]);
-          wv[3] = pack_bf16x2(pp[6], pp[7]);
-          bop[qb] = __builtin_bit_cast(bf16x8, wv);
+          bop[qb] = pack16x8<ET>(pp);
         }
         const int row_a = 32 * c + 4 * qg + (c16 >> 2);
         const int row_b = row_a + 16;
@@ -409,11 +404,11 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           const int chunk = 2 * db + ((c16 & 3) >> 1);
-          const i16x4 ta = lds_ld_tr16(vbuf_lds, v_off<BF16, DP>(row_a, chunk) + within);
-          const i16x4 tb = lds_ld_tr16(vbuf_lds, v_off<BF16, DP>(row_b, chunk) + within);
-          const bf16x8 vop = concat_bf16(ta, tb);
+          const i16x4 ta = lds_ld_tr16(vbuf_lds, v_off<H16, DP>(row_a, chunk) + within);
+          const i16x4 tb = lds_ld_tr16(vbuf_lds, v_off<H16, DP>(row_b, chunk) + within);
+          const u32x4 vop = concat16(ta, tb);
 #pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mfma_bf16(vop, bop[qb], acc[qb][db]);
+          for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mma16<ET>(vop, bop[qb], acc[qb][db]);
         }
       }
       if constexpr (GQA_PREFILL_SGB && C::NKB == 4 && C::QB == 2) {
@@ -525,57 +520,61 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       if constexpr (OUTF32) {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + d) = o;
       } else {
-        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        u32x2 pk = {pack16<ET>(o[0], o[1]), pack16<ET>(o[2], o[3])};
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d) = pk;
       }
     }
   }
 }
 
-template <bool BF16, int DP, bool DIRECT, bool MASKED, bool OUTF32>
+template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32>
 hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
-  using C = PreCfg<BF16, DP>;
+  using C = PreCfg<ET != kF32, DP>;
   const int HG = (a.g % 4 == 0) ? 4 : ((a.g % 2 == 0) ? 2 : 1);
   const int PB = (kWaves / HG) * C::RW;
   const int npb = (a.N + PB - 1) / PB;
   const int units = a.B * a.H_kv * (a.g / HG);
   const long blocks = (long)npb * units;
   const int xcd_major = (GQA_PREFILL_XCD_MAJOR && units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<BF16, DP, DIRECT, MASKED, OUTF32>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, stream, a, HG, units, npb, xcd_major);
   return hipGetLastError();
 }
 
-template <bool BF16, int DP, bool OUTF32>
+template <int ET, int DP, bool OUTF32>
 hipError_t launch_dp(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (BF16) {
+  if constexpr (ET != kF32) {
     if (a.D == DP) {
-      return a.mask ? launch_k<BF16, DP, true, true, OUTF32>(a, stream)
-                    : launch_k<BF16, DP, true, false, OUTF32>(a, stream);
+      return a.mask ? launch_k<ET, DP, true, true, OUTF32>(a, stream)
+                    : launch_k<ET, DP, true, false, OUTF32>(a, stream);
     }
   }
-  return a.mask ? launch_k<BF16, DP, false, true, OUTF32>(a, stream)
-                : launch_k<BF16, DP, false, false, OUTF32>(a, stream);
+  return a.mask ? launch_k<ET, DP, false, true, OUTF32>(a, stream)
+                : launch_k<ET, DP, false, false, OUTF32>(a, stream);
 }
 
-template <bool BF16, bool OUTF32>
+template <int ET, bool OUTF32>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (!BF16) {
-    if (a.D <= 16) return launch_dp<BF16, 16, OUTF32>(a, stream);
+  if constexpr (ET == kF32) {
+    if (a.D <= 16) return launch_dp<ET, 16, OUTF32>(a, stream);
   }
-  if (a.D <= 32) return launch_dp<BF16, 32, OUTF32>(a, stream);
-  if (a.D <= 64) return launch_dp<BF16, 64, OUTF32>(a, stream);
-  if (a.D <= 128) return launch_dp<BF16, 128, OUTF32>(a, stream);
-  return launch_dp<BF16, 256, OUTF32>(a, stream);
+  if (a.D <= 32) return launch_dp<ET, 32, OUTF32>(a, stream);
+  if (a.D <= 64) return launch_dp<ET, 64, OUTF32>(a, stream);
+  if (a.D <= 128) return launch_dp<ET, 128, OUTF32>(a, stream);
+  return launch_dp<ET, 256, OUTF32>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.in_bf16) {
-    return a.out_f32 ? launch_t<true, true>(a, stream) : launch_t<true, false>(a, stream);
+  switch (a.in_type) {
+    case kBF16:
+      return a.out_f32 ? launch_t<kBF16, true>(a, stream) : launch_t<kBF16, false>(a, stream);
+    case kF16:
+      return a.out_f32 ? launch_t<kF16, true>(a, stream) : launch_t<kF16, false>(a, stream);
+    default:
+      return launch_t<kF32, true>(a, stream);
   }
-  return launch_t<false, true>(a, stream);
 }
 
 }  // namespace gqa

@@ -31,9 +31,13 @@
  * out [B,H,N,D].  Scale is fixed at 1/sqrt(D).  Accumulation is fp32.
  *
  * Supported: all dims >= 1, H % H_kv == 0, 1 <= D <= 256,
- * D * sizeof(in_dtype) a multiple of 16 bytes (bf16: D % 8 == 0; fp32:
- * D % 4 == 0).  q, k, v, out and workspace must be 16-byte aligned.
+ * D * sizeof(in_dtype) a multiple of 16 bytes (bf16 and fp16: D % 8 == 0;
+ * fp32: D % 4 == 0).  q, k, v, out and workspace must be 16-byte aligned.
  * in_dtype is the type of q, k and v; out_dtype is in_dtype or GQA_F32.
+ * 16-bit inputs (bf16, fp16) run on the 16-bit matrix cores; the softmax
+ * weights are rounded to the input type for the P.V product, everything
+ * else accumulates in fp32.  fp16 is the cache precision named by the
+ * KV-cache figure of "Multi-Query Attention" (after *Implementation*).
  * Element counts must fit in a signed 64-bit integer and B*H*N, B*H_kv*M
  * must each stay below 2^31 rows.
  *
@@ -74,7 +78,8 @@ typedef enum {
 
 typedef enum {
   GQA_F32 = 0,  /* IEEE binary32                                              */
-  GQA_BF16 = 1  /* bfloat16; outputs are rounded to nearest, ties to even     */
+  GQA_BF16 = 1, /* bfloat16; outputs are rounded to nearest, ties to even     */
+  GQA_F16 = 2   /* IEEE binary16 (half); outputs rounded to nearest even      */
 } gqa_dtype_t;
 
 /*

@@ -10,8 +10,10 @@ import oracle
 
 # Tolerances (max abs error against the fp64 oracle run on the same,
 # already-rounded inputs): fp32 inputs 1e-4; bf16 inputs with fp32
-# accumulation 2e-2.
-TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# accumulation 2e-2; fp16 inputs 5e-3 (rounding the weights to fp16 costs at
+# most 2^-11 max|v|, about 2.4e-3 for N(0,1) values, and rounding an output
+# below 4 in magnitude at most 2^-9 = 2e-3).
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 5e-3}
 
 
 def np64(t):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa.h")
 
 OK, NULL, SHAPE, GROUP, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(10)
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 # fake, 16-byte aligned, non-overlapping "device" addresses: never dereferenced
 # because every call below fails validation first
@@ -95,6 +95,10 @@ def test_rejections_common(lib, fn):
     assert fn(lib, tin=7) == DTYPE
     assert fn(lib, tout=9) == DTYPE
     assert fn(lib, tin=F32, tout=BF16, D=128) == DTYPE   # fp32 in, bf16 out
+    assert fn(lib, tin=F16, tout=BF16) == DTYPE           # fp16 in, bf16 out
+    assert fn(lib, tin=BF16, tout=F16) == DTYPE
+    assert fn(lib, tin=F16, tout=F16, D=12) == UNSUP      # fp16 needs D % 8 == 0
+    assert fn(lib, tin=F32, tout=F16, D=128) == DTYPE
     assert fn(lib, D=264) == UNSUP
     assert fn(lib, D=12) == UNSUP                         # bf16 needs D % 8 == 0
     assert fn(lib, tin=F32, tout=F32, D=6) == UNSUP       # fp32 needs D % 4 == 0

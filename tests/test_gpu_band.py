@@ -45,6 +45,7 @@ SMALL = [
     (10, 1, 8, 2, 1000, 1000, 128, torch.bfloat16, 0, 0, 0, None),     # window 1: the own key
     (11, 2, 8, 2, 64, 640, 128, torch.bfloat16, 576, 127, 0, "blocks"),
     (12, 1, 3, 1, 150, 150, 32, torch.bfloat16, 0, 31, 0, None),       # g = 3
+    (13, 2, 8, 2, 300, 700, 128, torch.float16, 400, 99, 0, None),     # fp16 window + chunk
 ]
 
 

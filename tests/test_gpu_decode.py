@@ -50,6 +50,11 @@ SMALL = [
     (24, 2, 8, 8, 257, 128, torch.float32, "random"),
     (25, 1, 4, 1, 700, 256, torch.float32, None),
     (26, 2, 6, 2, 1500, 36, torch.float32, "blocks"),
+    (40, 2, 8, 2, 600, 128, torch.float16, None),         # fp16
+    (41, 2, 40, 2, 777, 64, torch.float16, "padding"),
+    (42, 1, 4, 1, 300, 256, torch.float16, None),
+    (43, 2, 6, 3, 130, 24, torch.float16, "random"),
+    (44, 4, 8, 2, 4097, 96, torch.float16, None),
 ]
 
 
@@ -63,6 +68,7 @@ def test_decode_peaky_scores():
     # q scaled x4 makes one key dominate and stresses the running-max rescale
     run_case(30, 2, 8, 2, 3000, 128, torch.bfloat16, None, q_scale=4.0)
     run_case(31, 2, 8, 2, 3000, 64, torch.float32, None, q_scale=4.0)
+    run_case(33, 2, 8, 2, 3000, 128, torch.float16, None, q_scale=4.0)
 
 
 def test_decode_fp32_output_of_bf16_inputs():
@@ -83,7 +89,7 @@ def test_decode_empty_rows_are_nan():
     compare(out, ref, TOL[torch.bfloat16], "empty rows")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("shape", [(2, 8, 2, 4096, 128), (1, 48, 3, 999, 64), (2, 4, 4, 70, 32)])
 def test_decode_head_mapping_bit_exact(dtype, shape):
     """K = 0 and V[b, j] = j: every score is 0, every weight 1, so query head
@@ -151,3 +157,13 @@ def test_decode_group_sweep_sampled(name):
     for b in (0, w.B - 1):
         ref = oracle_out(q[b:b + 1], k[b:b + 1], v[b:b + 1])
         compare(out[b:b + 1], ref, TOL[torch.bfloat16], f"{name} b={b}")
+
+
+def test_decode_mistral7b_fp16_full():
+    """The headline decode shape with fp16 inputs, every output element."""
+    w = workloads.by_name("decode_mistral7b_m4096_fp16")
+    q, k, v, mask, _ = workloads.make_inputs(w)
+    say("decode mistral7b fp16 full")
+    out = gqa.decode(*to_dev(q, k, v))
+    mx, rr = compare(out, oracle_out(q, k, v), TOL[torch.float16], w.name)
+    say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")

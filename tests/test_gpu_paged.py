@@ -48,6 +48,7 @@ SMALL = [
     (10, 2, 8, 2, 128, 256, 1000, torch.bfloat16, [1000, 999]),  # large blocks
     (11, 5, 32, 8, 128, 16, 5000, torch.bfloat16, "uniform"),  # several splits
     (12, 2, 4, 2, 256, 16, 700, torch.float32, "uniform"),     # fp32 D = 256
+    (13, 4, 32, 8, 128, 16, 3000, torch.float16, "uniform"),   # fp16
 ]
 
 

@@ -53,6 +53,11 @@ SMALL = [
     (24, 1, 8, 2, 40, 40, 128, torch.float32, None, True),
     (25, 1, 4, 1, 17, 33, 256, torch.float32, "blocks", False),
     (26, 2, 6, 3, 31, 200, 36, torch.float32, "random", True),
+    (40, 2, 8, 2, 130, 130, 128, torch.float16, None, True),      # fp16
+    (41, 1, 6, 3, 77, 200, 64, torch.float16, "padding", False),
+    (42, 1, 16, 2, 100, 100, 256, torch.float16, None, True),
+    (43, 2, 8, 4, 129, 129, 72, torch.float16, "random", True),
+    (44, 1, 3, 1, 40, 300, 32, torch.float16, "blocks", False),
 ]
 
 
@@ -64,6 +69,7 @@ def test_prefill_small(case):
 
 def test_prefill_peaky_scores():
     run_case(30, 1, 8, 2, 200, 200, 128, torch.bfloat16, None, True, q_scale=4.0)
+    run_case(32, 1, 8, 2, 200, 200, 128, torch.float16, None, True, q_scale=4.0)
     run_case(31, 1, 8, 2, 100, 150, 24, torch.float32, "padding", False, q_scale=4.0)
 
 
@@ -84,7 +90,7 @@ def test_prefill_empty_rows_are_nan():
     compare(out, ref, TOL[torch.bfloat16], "empty rows")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("shape", [(2, 8, 2, 100, 100, 128, True), (1, 6, 2, 65, 300, 32, False),
                                    (1, 4, 4, 33, 33, 64, True), (1, 12, 1, 20, 70, 128, False)])
 def test_prefill_head_mapping_bit_exact(dtype, shape):
@@ -128,12 +134,13 @@ def test_prefill_padded_d24_full():
     say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")
 
 
-def test_prefill_causal_n4096_full_sampled():
-    """Causal bf16 prefill (B4 H32 H_kv8 N=M=4096 D128) at full size, in the
-    launch configuration the benchmark times.  Sampled query rows of every
-    (batch row, head) are checked against the oracle, which evaluates a row
-    i as an explicit mask j <= i (causal == that mask is an oracle pin)."""
-    w = workloads.by_name("prefill_causal_n4096")
+@pytest.mark.parametrize("name", ["prefill_causal_n4096", "prefill_causal_n4096_fp16"])
+def test_prefill_causal_n4096_full_sampled(name):
+    """Causal prefill (B4 H32 H_kv8 N=M=4096 D128, bf16 and fp16) at full
+    size, in the launch configuration the benchmark times.  Sampled query rows
+    of every (batch row, head) are checked against the oracle, which evaluates
+    a row i as an explicit mask j <= i (causal == that mask is an oracle pin)."""
+    w = workloads.by_name(name)
     q, k, v, mask, causal = workloads.make_inputs(w)
     say("prefill causal full")
     out = gqa.prefill(*to_dev(q, k, v), causal=True).cpu()
@@ -145,5 +152,5 @@ def test_prefill_causal_n4096_full_sampled():
         m[:, r, : i + 1] = True
     for b in range(q.shape[0]):
         ref = oracle.gqa(np64(qs[b:b + 1]), np64(k[b:b + 1]), np64(v[b:b + 1]), np64(m[b:b + 1]))
-        mx, rr = compare(out[b:b + 1, :, rows, :], ref, TOL[torch.bfloat16], f"{w.name} b={b}")
+        mx, rr = compare(out[b:b + 1, :, rows, :], ref, TOL[w.torch_dtype], f"{w.name} b={b}")
         say(f"  b={b} max abs err {mx:.3e} rel rms {rr:.3e}")

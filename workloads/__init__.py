@@ -8,7 +8,7 @@ that defines a workload.
 Recipe (same bits for both sides):
   * a CPU ``torch.Generator`` seeded with the workload's seed;
   * draw q, then k, then v as float32 N(0, 1) in that order;
-  * cast to bfloat16 for bf16 workloads (round-to-nearest-even);
+  * cast to bfloat16 or float16 for 16-bit workloads (round-to-nearest-even);
   * padded workloads then draw one length per batch row, uniform on
     {1, ..., M}, and key j is valid for batch row b iff j < len_b.
 
@@ -63,7 +63,7 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+        return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[self.dtype]
 
 
 WORKLOADS = [
@@ -82,6 +82,10 @@ WORKLOADS = [
     # causal over M = 4096
     Workload("prefill_chunk512_m4096", 9, 16, 32, 8, 512, 4096, 128, "bf16",
              q_offset=3584, window_right=0),
+    # the headline decode and causal prefill shapes with fp16 inputs
+    Workload("decode_mistral7b_m4096_fp16", 10, 16, 32, 8, 1, 4096, 128, "fp16"),
+    Workload("prefill_causal_n4096_fp16", 11, 4, 32, 8, 4096, 4096, 128, "fp16",
+             causal=True),
 ]
 
 
@@ -104,7 +108,7 @@ def _draw(gen, B, H, H_kv, N, M, D, dtype):
     q = torch.randn((B, H, N, D), generator=gen, dtype=torch.float32)
     k = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
     v = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
-    if dtype == torch.bfloat16:
+    if dtype in (torch.bfloat16, torch.float16):
         q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
     return q, k, v
 
@@ -141,7 +145,7 @@ def random_case(seed, B, H, H_kv, N, M, D, dtype=torch.float32,
     q = torch.randn((B, H, N, D), generator=gen, dtype=torch.float32) * q_scale
     k = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
     v = torch.randn((B, H_kv, M, D), generator=gen, dtype=torch.float32)
-    if dtype == torch.bfloat16:
+    if dtype in (torch.bfloat16, torch.float16):
         q, k, v = q.to(dtype), k.to(dtype), v.to(dtype)
     mask = None
     if mask_kind == "padding":
@@ -186,7 +190,7 @@ class PagedWorkload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+        return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[self.dtype]
 
 
 PAGED_WORKLOADS = [
@@ -234,7 +238,7 @@ def random_paged_case(seed, B, H, H_kv, D, block_size, max_len, dtype=torch.floa
     q = torch.randn((B, H, 1, D), generator=gen, dtype=torch.float32) * q_scale
     kp = torch.randn((num_blocks, H_kv, block_size, D), generator=gen, dtype=torch.float32)
     vp = torch.randn((num_blocks, H_kv, block_size, D), generator=gen, dtype=torch.float32)
-    if dtype == torch.bfloat16:
+    if dtype in (torch.bfloat16, torch.float16):
         q, kp, vp = q.to(dtype), kp.to(dtype), vp.to(dtype)
     perm = torch.randperm(num_blocks, generator=gen)
     table = torch.full((B, max_blocks), -1, dtype=torch.int32)
