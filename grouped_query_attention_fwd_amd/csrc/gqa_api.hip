@@ -101,6 +101,25 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
       (plan.workspace_bytes > 0 && overlaps(out, ob, workspace, plan.workspace_bytes)))
     return GQA_ERR_ALIAS;
 
+  if (plan.wide) {
+    // the group's heads as the query rows of a prefill over the same K/V:
+    // q [B, H, 1, D] is [B, H_kv, g, D]; the [B, 1, M] mask serves every row
+    gqa::PrefillArgs p{};
+    p.q = q; p.k = k; p.v = v; p.mask = mask; p.out = out;
+    p.B = B; p.H = H_kv; p.H_kv = H_kv; p.N = H / H_kv; p.M = M; p.D = D;
+    p.g = 1;
+    p.q_offset = 0; p.wl = -1; p.wr = -1;
+    p.mask_rs = 0;
+    p.mask_bs = M;
+    p.splits = plan.wide_splits;
+    p.kps = plan.wide_kps;
+    p.partials = plan.workspace_bytes > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
+    p.in_type = (int)in_dtype;
+    p.out_f32 = out_dtype == GQA_F32;
+    if (gqa::launch_prefill(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
+    return GQA_OK;
+  }
+
   gqa::DecodeArgs a{};
   a.q = q; a.k = k; a.v = v; a.mask = mask; a.out = out;
   a.B = B; a.H = H; a.H_kv = H_kv; a.M = M; a.D = D;
@@ -199,6 +218,10 @@ gqa_status_t gqa_prefill_band(const void* q, const void* k, const void* v, const
   a.q_offset = q_offset;
   a.wl = window_left < 0 ? -1 : window_left;
   a.wr = window_right < 0 ? -1 : window_right;
+  a.mask_rs = M;
+  a.mask_bs = (long long)N * M;
+  a.splits = 1;
+  a.kps = M;
   a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (gqa::launch_prefill(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;

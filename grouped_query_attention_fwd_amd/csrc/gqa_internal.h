@@ -45,6 +45,16 @@ struct PrefillArgs {
   //   (wl < 0 || j >= i + q_offset - wl) && (wr < 0 || j <= i + q_offset + wr).
   // Causal (top-left) is q_offset = 0, wl = -1, wr = 0.
   int q_offset, wl, wr;
+  // mask strides in bytes: rows M and batch rows N * M for a [B, N, M]
+  // mask; rows 0 and batch rows M when one [B, 1, M] row serves every query
+  int mask_rs;
+  long long mask_bs;
+  // key splits: with splits > 1 workgroup column s covers keys
+  // [s * kps, (s + 1) * kps) (kps a multiple of 64) and writes a partial
+  // (m, l, acc) per query row to partials [B * H * N][splits][D + 4] fp32; a
+  // second kernel merges them
+  int splits, kps;
+  float* partials;
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };
@@ -52,6 +62,10 @@ struct PrefillArgs {
 // Split plan shared by the workspace query and the decode launch, so both
 // agree for the same shapes.
 struct DecodePlan {
+  // wide: large groups (more than 32 heads) run as a prefill with the group's
+  // heads as query rows (one shared K/V tile stream per (b, KV head)), split
+  // over keys into wide_splits ranges of wide_kps keys
+  int wide, wide_splits, wide_kps;
   int head_chunk;
   int head_chunks;
   int xcd_group;

@@ -172,7 +172,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   const size_t kv_base = ((size_t)b * a.H_kv + j) * (size_t)M * D;
   const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
   const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
-  const uint8_t* mb = MASKED ? a.mask + (size_t)b * N * M : nullptr;
+  const uint8_t* mb = MASKED ? a.mask + (size_t)b * a.mask_bs : nullptr;
+  const size_t mrs = MASKED ? (size_t)a.mask_rs : 0;   // mask row stride
   const float sl = kLog2e / sqrtf((float)D);
 
   // Band edges of query position pos, clamped to [0, M]: keys
@@ -188,15 +189,17 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     const long long x = (long long)pos + a.q_offset + a.wr + 1;
     return (int)(x < 0 ? 0 : (x > M ? M : x));
   };
-  // key range of the workgroup and of this wave
+  // key range of the workgroup and of this wave, within this key split
+  const int s_lo = (int)blockIdx.y * a.kps;
+  const int s_hi = min(M, s_lo + a.kps);
   const int last_pos = min(N, p0 + PB);          // exclusive
-  const int kbeg = key_lo(p0);
-  const int kend = (p0 < N) ? key_hi(last_pos - 1) : 0;
+  const int kbeg = max(key_lo(p0), s_lo);
+  const int kend = (p0 < N) ? min(key_hi(last_pos - 1), s_hi) : 0;
   const int t_first = kbeg / C::BN;
   const int ntiles = (kend + C::BN - 1) / C::BN;
   const int w_last = min(N, wp0 + C::RW);        // exclusive
-  const int w_kbeg = key_lo(wp0);
-  const int w_kend = (wp0 >= N) ? 0 : key_hi(w_last - 1);
+  const int w_kbeg = max(key_lo(wp0), s_lo);
+  const int w_kend = (wp0 >= N) ? 0 : min(key_hi(w_last - 1), s_hi);
   // keys every row of this wave sees: [w_full_lo, w_full_hi)
   const int w_full_lo = (wp0 >= N) ? M : key_lo(w_last - 1);
   const int w_full_hi = (wp0 >= N) ? 0 : key_hi(wp0);
@@ -236,7 +239,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int key = k0 + (idx - i * C::BN);
       const int pos = p0 + i;
       if (pos < N && key < kend && key >= key_lo(pos) && key < key_hi(pos) &&
-          mb[(size_t)pos * M + key])
+          mb[(size_t)pos * mrs + key])
         any = 1;
     }
     return __syncthreads_or(any) != 0;
@@ -339,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
           const int key = k0 + 16 * kb + 4 * qg + r;
           bool vis = key >= lo && key < hi;
           if constexpr (MASKED) {
-            const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * M + min(key, M - 1)];
+            const uint8_t mbyte = mb[(size_t)min(pos, N - 1) * mrs + min(key, M - 1)];
             vis = vis && (mbyte != 0) && (pos < N);
           }
           sc[qb][kb][r] = vis ? sc[qb][kb][r] : kNegInf;
@@ -501,12 +504,28 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     t = tn;
   }
 
-  // ---- epilogue: O = acc / l ------------------------------------------------
+  // ---- epilogue: O = acc / l, or the partial of this key split -------------
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const float lt = rows_sum(l_run[qb]);
     const int pos = wp0 + 16 * qb + c16;
     if (pos >= N) continue;
+    if (a.splits > 1) {
+      // record [m, l, -, -, acc[0..D)] of this row and split; m is the
+      // softmax reference the weights were taken against
+      const size_t row = ((size_t)b * a.H + h) * N + pos;
+      float* part = a.partials + (row * a.splits + blockIdx.y) * (size_t)(D + 4);
+      if (qg == 0) {
+        part[0] = m_run[qb];
+        part[1] = lt;
+      }
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int d = 16 * db + 4 * qg;
+        if (d < D) *reinterpret_cast<f32x4*>(part + 4 + d) = acc[qb][db];
+      }
+      continue;
+    }
     const size_t obase = (((size_t)b * a.H + h) * N + pos) * (size_t)D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -527,6 +546,56 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   }
 }
 
+// Merge the key-split partials of every query row, in split order, eight
+// splits per memory round trip (indexes clamped to the last split): a
+// running m*, with o = sum_s acc_s 2^((m_s - m*) sl) / sum_s l_s 2^((m_s - m*) sl).
+constexpr int kMergeThreads = 128;
+template <int ET, bool OUTF32>
+__global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArgs a) {
+  const size_t row = blockIdx.x;
+  const int d = blockIdx.y * kMergeThreads + threadIdx.x;
+  if (d >= a.D) return;
+  const float sl = kLog2e / sqrtf((float)a.D);
+  const size_t stride = (size_t)a.D + 4;
+  const int S = a.splits;
+  const float* p = a.partials + row * S * stride;
+  float mx = kNegInf, L = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float pm[8], pl[8], pa[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t o = (size_t)min(s0 + u, S - 1) * stride;
+      pm[u] = p[o];
+      pl[u] = p[o + 1];
+      pa[u] = p[o + 4 + d];
+    }
+    float cm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) cm = fmaxf(cm, pm[u]);
+    const float nm = fmaxf(mx, cm);
+    if (nm == kNegInf) continue;                 // nothing visible yet
+    const float f0 = (mx == kNegInf) ? 0.f : exp2_hw((mx - nm) * sl);
+    L *= f0;
+    A *= f0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < S) {
+        const float f = exp2_hw((pm[u] - nm) * sl);
+        L = fmaf(pl[u], f, L);
+        A = fmaf(pa[u], f, A);
+      }
+    }
+    mx = nm;
+  }
+  const float o = A / L;
+  if constexpr (OUTF32) {
+    reinterpret_cast<float*>(a.out)[row * a.D + d] = o;
+  } else {
+    reinterpret_cast<uint16_t*>(a.out)[row * a.D + d] = cvt16<ET>(o);
+  }
+}
+
 template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32>
 hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   using C = PreCfg<ET != kF32, DP>;
@@ -536,8 +605,15 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * (a.g / HG);
   const long blocks = (long)npb * units;
   const int xcd_major = (GQA_PREFILL_XCD_MAJOR && units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, stream, a, HG, units, npb, xcd_major);
+  hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32>),
+                     dim3((unsigned)blocks, (unsigned)a.splits), dim3(kThreads), 0, stream, a, HG,
+                     units, npb, xcd_major);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const long rows = (long)a.B * a.H * a.N;
+  hipLaunchKernelGGL((prefill_merge_kernel<ET, OUTF32>),
+                     dim3((unsigned)rows, (unsigned)((a.D + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -90,7 +90,8 @@ def test_decode_empty_rows_are_nan():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-@pytest.mark.parametrize("shape", [(2, 8, 2, 4096, 128), (1, 48, 3, 999, 64), (2, 4, 4, 70, 32)])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 4096, 128), (1, 48, 3, 999, 64), (2, 4, 4, 70, 32),
+                                   (2, 64, 2, 777, 128), (1, 64, 1, 3000, 64)])
 def test_decode_head_mapping_bit_exact(dtype, shape):
     """K = 0 and V[b, j] = j: every score is 0, every weight 1, so query head
     h must return exactly h // g (repeat-interleave, not tiling)."""
