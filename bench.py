@@ -64,12 +64,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_only(text):
+    """C/HIP source with comments removed and whitespace runs collapsed, so
+    that a comment edit does not count as a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_sha(kind):
     h = hashlib.sha256()
     for p in (KERNEL_SOURCES[kind],
               os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "gqa_device.h")):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,7 +13,9 @@
 //
 // Work split: one workgroup of four waves per (batch row, KV head, chunk of
 // up to 16 query heads, key range "split").  Inside a workgroup the waves
-// take interleaved chunks of KC keys.  Per chunk a wave
+// take interleaved chunks of KC keys, addressed per aligned group of 16 keys
+// (contiguous rows, or one block-table entry of a paged cache, in which case
+// each sequence's own length ends its key range).  Per chunk a wave
 //   1. loads K rows straight into MFMA operand registers (16 bytes per lane)
 //      and V rows with coalesced 16-byte loads, all issued up front with
 //      clamped (always valid) addresses so nothing waits on a branch;
@@ -24,12 +26,14 @@
 //      rescale factor stay in the lane and the row max needs two cross-lane
 //      steps;
 //   5. forms O^T += V^T P^T on the matrix cores, reading V^T from LDS with
-//      the transposing ds_read_b64_tr_b16 (bf16) or plain reads (fp32).
+//      the transposing ds_read_b64_tr_b16 (16-bit) or plain reads (fp32).
 // The four waves merge (m, l, acc) through LDS.  With one split the result is
 // written directly.  Otherwise every workgroup stores its (m, l, acc) partial
 // to the fp32 workspace and a second small kernel merges the splits of each
 // head in split order.  The merge order is fixed, so results are
 // bit-reproducible, and no cross-workgroup synchronisation is needed.
+// Groups of more than 32 heads (contiguous cache) go through the prefill
+// kernel instead, with the heads as query rows (see plan_decode).
 #include "gqa_device.h"
 #include "gqa_internal.h"
 

@@ -15,30 +15,34 @@
 //     share a block of positions (HG heads x PB positions, HG in {4,2,1});
 //     the K/V tiles it streams are therefore read once for all of its heads
 //     (the zero head stride of "Multi-Query Attention", *Implementation*) and
-//     all heads share one causal / mask frontier.
-//   * K and V tiles of BN keys are double-buffered in LDS.  bf16 tiles whose
-//     rows need no column padding go straight from global memory to LDS with
-//     global_load_lds_dwordx4 (no staging registers); the XOR swizzle of the
-//     LDS rows is applied by permuting each lane's global source.  Other
-//     cases stage through registers.  The next tile's copy is issued before
-//     the current tile's math, so its latency hides behind the MFMAs.
+//     all heads share one band / mask frontier.
+//   * K and V tiles of BN keys are double-buffered in LDS, as four distinct
+//     LDS objects with the tile loop unrolled by two (every access names its
+//     stage).  16-bit tiles whose rows need no column padding go straight
+//     from global memory to LDS with global_load_lds_dwordx4 (no staging
+//     registers); the XOR swizzle of the LDS rows is applied by permuting
+//     each lane's global source.  Other cases stage through registers.  The
+//     next tile's copy is issued before the current tile's math.
 //   * Each wave owns 16*QB query rows.  S^T = K Q^T and O^T = V^T P^T run on
-//     v_mfma_f32_16x16x32_bf16 (bf16 inputs) or v_mfma_f32_16x16x4f32 (fp32
-//     inputs); V^T is read with the transposing ds_read_b64_tr_b16.  P is
-//     rounded to bf16 (v_cvt_pk_bf16_f32) for the bf16 product; all
+//     v_mfma_f32_16x16x32_bf16 / _f16 (16-bit inputs) or
+//     v_mfma_f32_16x16x4f32 (fp32 inputs); V^T is read with the transposing
+//     ds_read_b64_tr_b16.  P is rounded to the input type
+//     (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32) for the 16-bit product; all
 //     accumulation is fp32.
 //   * Online softmax per query row with exp2 and a scale of log2(e)/sqrt(D);
 //     a lane owns one query row per 16-row block, so its running max and
 //     rescale factor never leave the lane.
-//   * Causal: tiles past the block's last position are never visited and a
-//     wave skips tiles past its own rows; only tiles that cross the diagonal,
-//     the end of the keys or a mask pay for per-element visibility.  Mask:
-//     tiles with no visible pair are skipped entirely (no K/V copy, no MFMA),
-//     decided by a workgroup-wide vote.
-//   * Causal blocks are dispatched heaviest first; consecutive workgroups
-//     cycle through (batch row, KV head) units, so with a unit count that is
-//     a multiple of 8 every block of one unit lands on the same XCD and its
-//     K/V stay in that XCD's L2.
+//   * Band (causal is the band with right edge 0): each workgroup and wave
+//     derive their key range from it, tiles outside it are never visited,
+//     and only tiles that cross a band edge, the end of the keys or a mask
+//     pay for per-element visibility.  Mask: tiles with no visible pair are
+//     skipped entirely (no K/V copy, no MFMA), decided by a workgroup vote.
+//   * Dispatch: workgroup L runs on XCD L % 8; each XCD walks its own units
+//     one after another (all position blocks of a unit together, heaviest
+//     causal blocks first), so the tiles in flight on an XCD stay in its L2.
+//   * Optional key splits (used by the decode of large groups, whose heads
+//     are the query rows here): workgroup column s covers one key range and
+//     writes a partial (m, l, acc) per row; a small kernel merges them.
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
