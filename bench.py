@@ -52,11 +52,10 @@ KERNEL_SOURCES = {
     "decode_paged": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
     "prefill": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "prefill.hip"),
 }
-# the kernels one call launches (decode: main kernel, then the split merge)
-KERNEL_NAMES = {"decode": "decode_kernel+decode_merge_kernel",
-                "decode_paged": "decode_kernel+decode_merge_kernel", "prefill": "prefill_kernel"}
-KERNEL_PATTERNS = {"decode": ("decode_kernel", "decode_merge_kernel"),
-                   "decode_paged": ("decode_kernel", "decode_merge_kernel"),
+# the kernel one call launches (the decode merges its key splits inside the kernel)
+KERNEL_NAMES = {"decode": "decode_kernel", "decode_paged": "decode_kernel",
+                "prefill": "prefill_kernel"}
+KERNEL_PATTERNS = {"decode": ("decode_kernel",), "decode_paged": ("decode_kernel",),
                    "prefill": ("prefill_kernel",)}
 
 
@@ -145,13 +144,13 @@ def make_call(info, torch):
     ops = []
     if info["kind"] == "decode_paged":
         mb = info["sets"][0][3].shape[1]
-        ws = torch.empty(max(1, gqa.decode_paged_workspace_size(w.B, w.H, w.H_kv, mb,
+        ws = torch.zeros(max(1, gqa.decode_paged_workspace_size(w.B, w.H, w.H_kv, mb,
                                                                 w.block_size, w.D)),
                          dtype=torch.uint8, device="cuda")
         for (q, kp, vp, bt, kl) in info["sets"]:
             ops.append(gqa.decode_paged_op(q, kp, vp, bt, kl, workspace=ws))
     elif w.kind == "decode":
-        ws = torch.empty(max(1, gqa.decode_workspace_size(w.B, w.H, w.H_kv, w.M, w.D)),
+        ws = torch.zeros(max(1, gqa.decode_workspace_size(w.B, w.H, w.H_kv, w.M, w.D)),
                          dtype=torch.uint8, device="cuda")
         for (q, k, v, m) in info["sets"]:
             ops.append(gqa.decode_op(q, k, v, m, workspace=ws))

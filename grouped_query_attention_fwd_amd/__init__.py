@@ -35,7 +35,11 @@ import os
 __all__ = ["decode", "decode_paged", "prefill", "prefill_band", "decode_op", "decode_paged_op",
            "prefill_op", "prefill_band_op",
            "decode_workspace_size", "decode_paged_workspace_size", "status_string",
-           "library_path", "GQAError", "load_library"]
+           "library_path", "GQAError", "load_library", "DECODE_COUNTER_BYTES"]
+
+# Bytes of arrival counters at the start of a decode workspace; they must be
+# zero before the first call, and every call leaves them zero.
+DECODE_COUNTER_BYTES = 1024
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
@@ -167,7 +171,38 @@ def _out(q, out, out_dtype, shape):
     return out
 
 
-def _prepare_decode(q, k, v, mask, out, out_dtype, workspace):
+# Decode workspaces kept per (device, stream) for the one-shot calls,
+# zero-filled when allocated.  Every decode call leaves the counter area zero
+# again, so calls queued on one stream can share one buffer; calls on
+# different streams get different buffers.  A buffer only grows (a larger,
+# zeroed one replaces it).
+_STREAM_WS = {}
+_STREAM_WS_MAX = 16
+
+
+def _stream_workspace(device, need):
+    torch = _torch()
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _STREAM_WS.get(key)
+    if ws is None or ws.numel() < need:
+        with torch.cuda.device(device):
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _STREAM_WS.pop(key, None)
+        if len(_STREAM_WS) >= _STREAM_WS_MAX:
+            _STREAM_WS.pop(next(iter(_STREAM_WS)))
+        _STREAM_WS[key] = ws
+    return ws
+
+
+def _workspace(q, need, workspace, shared):
+    if workspace is not None or need == 0:
+        return workspace
+    if shared:
+        return _stream_workspace(q.device, need)
+    return _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+
+
+def _prepare_decode(q, k, v, mask, out, out_dtype, workspace, shared=False):
     torch = _torch()
     _check_tensors(q, k, v, mask)
     B, H, N, D = q.shape
@@ -179,8 +214,7 @@ def _prepare_decode(q, k, v, mask, out, out_dtype, workspace):
     out = _out(q, out, out_dtype, (B, H, 1, D))
     lib = load_library()
     need = int(lib.gqa_decode_workspace_size(B, H, H_kv, M, D))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(q, need, workspace, shared)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask), out.data_ptr(),
@@ -188,7 +222,8 @@ def _prepare_decode(q, k, v, mask, out, out_dtype, workspace):
     return lib, args, out, workspace
 
 
-def _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out, out_dtype, workspace):
+def _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out, out_dtype, workspace,
+                          shared=False):
     torch = _torch()
     _check_tensors(q, k_pool, v_pool, None, same_batch=False)
     B, H, N, D = q.shape
@@ -208,8 +243,7 @@ def _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out, out_dtype
     out = _out(q, out, out_dtype, (B, H, 1, D))
     lib = load_library()
     need = int(lib.gqa_decode_paged_workspace_size(B, H, H_kv, max_blocks, block_size, D))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(q, need, workspace, shared)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
@@ -295,10 +329,12 @@ def prefill_band_op(q, k, v, mask=None, q_offset=0, window_left=-1, window_right
 
 def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
     """One decode step; see the module docstring.  workspace: optional
-    uint8 device tensor of at least decode_workspace_size(...) bytes (no
-    initialisation needed); allocated per call when omitted."""
+    uint8 device tensor of at least decode_workspace_size(...) bytes whose
+    first DECODE_COUNTER_BYTES bytes are zero before its first use (every
+    call leaves them so).  When omitted, a buffer kept for the current
+    stream is used."""
     torch = _torch()
-    lib, args, out, _ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace)
+    lib, args, out, _ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace, shared=True)
     with torch.cuda.device(q.device):
         _check(lib.gqa_decode(*args, torch.cuda.current_stream(q.device).cuda_stream))
     return out
@@ -311,7 +347,7 @@ def decode_paged(q, k_pool, v_pool, block_table, kv_len, out=None, out_dtype=Non
     keys t < kv_len[b] exist.  Workspace as for decode()."""
     torch = _torch()
     lib, args, out, _ws = _prepare_decode_paged(q, k_pool, v_pool, block_table, kv_len, out,
-                                                out_dtype, workspace)
+                                                out_dtype, workspace, shared=True)
     with torch.cuda.device(q.device):
         _check(lib.gqa_decode_paged(*args, torch.cuda.current_stream(q.device).cuda_stream))
     return out

@@ -29,9 +29,10 @@
 //      the transposing ds_read_b64_tr_b16 (16-bit) or plain reads (fp32).
 // The four waves merge (m, l, acc) through LDS.  With one split the result is
 // written directly.  Otherwise every workgroup stores its (m, l, acc) partial
-// to the fp32 workspace and a second small kernel merges the splits of each
-// head in split order.  The merge order is fixed, so results are
-// bit-reproducible, and no cross-workgroup synchronisation is needed.
+// to the fp32 workspace and takes a ticket from the unit's arrival counter;
+// the workgroup that arrives last merges the unit's splits in split order
+// (so the result is bit-reproducible whichever finishes last), then sets the
+// partials and the counter back to zero.
 // Groups of more than 32 heads (contiguous cache) go through the prefill
 // kernel instead, with the heads as query rows (see plan_decode).
 #include "gqa_device.h"
@@ -65,6 +66,8 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #ifndef GQA_DECODE_PAGED_TARGET_WGS
 #define GQA_DECODE_PAGED_TARGET_WGS 256
 #endif
+static_assert(GQA_DECODE_TARGET_WGS <= kMaxCounters && GQA_DECODE_PAGED_TARGET_WGS <= kMaxCounters,
+              "a split plan needs fewer units than the counter area holds");
 
 template <bool H16, int DP>
 struct DecCfg {
@@ -110,6 +113,96 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float x) {
   } else {
     static_assert(ET != kF32, "fp32 inputs have fp32 outputs");
     reinterpret_cast<uint16_t*>(out)[idx] = cvt16<ET>(x);
+  }
+}
+
+// Four consecutive output elements idx .. idx + 3 (idx a multiple of 4).
+template <int ET, bool OUTF32>
+__device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 x) {
+  if constexpr (OUTF32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = x;
+  } else {
+    const u32x2 pk = {pack16<ET>(x[0], x[1]), pack16<ET>(x[2], x[3])};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) = pk;
+  }
+}
+
+// Key-split partials of one unit: [splits][16 heads][D + 4] fp32 rows of
+// (m, l, -, -, acc[0..D)), m being the score maximum (unscaled) the weights
+// were taken against.  Byte offset of row (split, head):
+__device__ __forceinline__ uint32_t part_row(int split, int hh, int D) {
+  return (uint32_t)((split * 16 + hh) * (D + 4)) * 4u;
+}
+
+// Merge the key-split partials of one (batch row, KV head, head chunk):
+// m* = max_s m_s, o = sum_s acc_s 2^((m_s - m*) sl) / sum_s l_s 2^((m_s - m*) sl),
+// taken over the splits in order, SB splits per memory round trip with a
+// running m*, so the result does not depend on which split finished last.
+// A thread owns quads (head, 4 consecutive d) tid, tid + kThreads, ...,
+// QPT of them per round trip; every load of a round trip is issued before
+// any of its arithmetic.
+template <int ET, bool OUTF32, int QPT, int SB>
+__device__ __forceinline__ void merge_quads(const DecodeArgs& a, __amdgpu_buffer_rsrc_t prs, int b,
+                                            int h0, int gh, int tid) {
+  const int D = a.D, DQ = a.D >> 2, S = a.splits;
+  const int nq = gh * DQ;
+  const float sl = kLog2e / sqrtf((float)D);
+  for (int q0 = tid; q0 < nq; q0 += QPT * kThreads) {
+    int hh[QPT], d[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int q = min(q0 + i * kThreads, nq - 1);  // clamped: loads stay valid
+      hh[i] = q / DQ;
+      d[i] = 4 * (q - hh[i] * DQ);
+    }
+    float mx[QPT], L[QPT];
+    f32x4 A[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      mx[i] = kNegInf;
+      L[i] = 0.f;
+      A[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s0 = 0; s0 < S; s0 += SB) {
+      f32x2 ml[QPT][SB];
+      f32x4 pa[QPT][SB];
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const uint32_t ro = part_row(min(s0 + u, S - 1), hh[i], D);
+          ml[i][u] = ld_dev2(prs, ro);
+          pa[i][u] = ld_dev4(prs, ro + 16 + 4 * d[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        float cm = kNegInf;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) cm = fmaxf(cm, ml[i][u][0]);  // clamped copies change nothing
+        const float nm = fmaxf(mx[i], cm);
+        if (nm != kNegInf) {  // else nothing visible yet
+          const float f0 = (mx[i] == kNegInf) ? 0.f : exp2_hw((mx[i] - nm) * sl);
+          L[i] *= f0;
+          A[i] *= f0;
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            if (s0 + u < S) {
+              const float f = exp2_hw((ml[i][u][0] - nm) * sl);
+              L[i] = fmaf(ml[i][u][1], f, L[i]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) A[i][e] = fmaf(pa[i][u][e], f, A[i][e]);
+            }
+          }
+          mx[i] = nm;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      if (q0 + i * kThreads < nq)
+        store_out4<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh[i]) * D + d[i], A[i] / L[i]);
+    }
   }
 }
 
@@ -391,97 +484,64 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   }
   __syncthreads();
 
-  const int ne = gh * D;
+  // Each thread combines the four waves for quads (head, 4 consecutive d).
+  const int DQ = D >> 2;  // D % 4 == 0 for every supported type
+  const int nq = gh * DQ;
   const bool single = (a.splits == 1);
-  float* part = single ? nullptr
-                       : a.partials + ((size_t)unit * a.splits + s) * 16 * (size_t)(D + 2);
-  for (int idx = tid; idx < ne; idx += kThreads) {
-    const int hh = idx / D;
-    const int d = idx - hh * D;
+  const __amdgpu_buffer_rsrc_t prs = raw_rsrc(
+      single ? a.out : a.partials + (size_t)unit * a.splits * 16 * (D + 4),
+      single ? 0u : part_row(a.splits, 0, D));
+  for (int q = tid; q < nq; q += kThreads) {
+    const int hh = q / DQ;
+    const int d = 4 * (q - hh * DQ);
     float mx = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, cm[ww * 16 + hh]);
     const float mu = (mx == kNegInf) ? 0.f : mx;
-    float L = 0.f, A = 0.f;
+    float L = 0.f;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const float f = exp2_hw((cm[ww * 16 + hh] - mu) * sl);
       L = fmaf(cl[ww * 16 + hh], f, L);
-      A = fmaf(cacc[(ww * 16 + hh) * DP + d], f, A);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(cacc + (ww * 16 + hh) * DP + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A[e] = fmaf(c[e], f, A[e]);
     }
     if (single) {
-      store_out<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+      store_out4<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
     } else {
-      float* ph = part + (size_t)hh * (D + 2);
-      if (d == 0) {
-        ph[0] = mx;
-        ph[1] = L;
-      }
-      ph[2 + d] = A;
+      const uint32_t ro = part_row(s, hh, D);
+      st_dev4(prs, ro + 16 + 4 * d, A);
+      if (d == 0) st_dev2(prs, ro, f32x2{mx, L});
     }
   }
-}
+  if (single) return;
 
-// Merge the per-split partials of one (batch row, KV head, head chunk):
-// m* = max_s m_s, o = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*),
-// in split order.  One thread per output element; blockIdx.y walks the
-// (head, d) elements of a unit in blocks of kMergeThreads.
-constexpr int kMergeThreads = 128;
-// MAXS > 0: at most MAXS splits; every partial is loaded up front (indexes
-// clamped to the last split) so the loads overlap.  MAXS == 0: any count.
-template <int ET, bool OUTF32, int MAXS>
-__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a) {
-  const int unit = blockIdx.x;
-  const int per_b = a.H_kv * a.head_chunks;
-  const int b = unit / per_b;
-  const int rem = unit - b * per_b;
-  const int j = rem / a.head_chunks;
-  const int hc = rem - j * a.head_chunks;
-  const int h0 = j * a.g + hc * a.head_chunk;
-  const int gh = min(a.head_chunk, a.g - hc * a.head_chunk);
-  const int D = a.D;
-  const int idx = blockIdx.y * kMergeThreads + threadIdx.x;
-  if (idx >= gh * D) return;
-  const int hh = idx / D;
-  const int d = idx - hh * D;
-  const float sl = kLog2e / sqrtf((float)D);
-  const size_t stride = 16 * (size_t)(D + 2);
-  const int S = a.splits;
-  const float* ph = a.partials + (size_t)unit * S * stride + (size_t)hh * (D + 2);
-  float L = 0.f, A = 0.f;
-  if constexpr (MAXS > 0) {
-    float pm[MAXS], pl[MAXS], pa[MAXS];
-#pragma unroll
-    for (int ss = 0; ss < MAXS; ++ss) {
-      const float* p = ph + (size_t)min(ss, S - 1) * stride;
-      pm[ss] = p[0];
-      pl[ss] = p[1];
-      pa[ss] = p[2 + d];
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int ss = 0; ss < MAXS; ++ss) mx = fmaxf(mx, pm[ss]);  // clamped copies change nothing
-    const float mu = (mx == kNegInf) ? 0.f : mx;
-#pragma unroll
-    for (int ss = 0; ss < MAXS; ++ss) {
-      if (ss < S) {
-        const float f = exp2_hw((pm[ss] - mu) * sl);
-        L = fmaf(pl[ss], f, L);
-        A = fmaf(pa[ss], f, A);
-      }
-    }
-  } else {
-    float mx = kNegInf;
-    for (int ss = 0; ss < S; ++ss) mx = fmaxf(mx, ph[ss * stride]);
-    const float mu = (mx == kNegInf) ? 0.f : mx;
-    for (int ss = 0; ss < S; ++ss) {
-      const float* p = ph + ss * stride;
-      const float f = exp2_hw((p[0] - mu) * sl);
-      L = fmaf(p[1], f, L);
-      A = fmaf(p[2 + d], f, A);
-    }
+  // ---- the last split of the unit to arrive merges all of them -----------
+  // Partials are stored and loaded with device-scope accesses, which bypass
+  // the non-coherent parts of the per-XCD L2s, so no L2 write-back or
+  // invalidation is needed: each wave waits until its stores are complete
+  // before the workgroup takes its ticket, and the last workgroup loads the
+  // partials only after its ticket shows every split has arrived.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __shared__ int s_last;
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned t = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (t == (unsigned)a.splits - 1u);
   }
-  store_out<ET, OUTF32>(a.out, ((size_t)b * a.H + h0 + hh) * D + d, A / L);
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) st_dev(a.counters + unit, 0u);  // ready for the next call
+  if (a.splits <= 2) {
+    merge_quads<ET, OUTF32, 4, 2>(a, prs, b, h0, gh, tid);
+  } else if (a.splits <= 4) {
+    merge_quads<ET, OUTF32, 2, 4>(a, prs, b, h0, gh, tid);
+  } else {
+    merge_quads<ET, OUTF32, 1, 8>(a, prs, b, h0, gh, tid);
+  }
 }
 
 template <int ET, int DP, bool EXACT, bool OUTF32>
@@ -494,17 +554,6 @@ hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, true, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
-  const int per_unit = (a.head_chunk * a.D + kMergeThreads - 1) / kMergeThreads;
-  const dim3 mgrid(units, per_unit);
-  if (a.splits <= 2) {
-    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 2>), mgrid, dim3(kMergeThreads), 0, stream, a);
-  } else if (a.splits <= 8) {
-    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 8>), mgrid, dim3(kMergeThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((decode_merge_kernel<ET, OUTF32, 0>), mgrid, dim3(kMergeThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -553,8 +602,10 @@ DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
   p.splits = (int)splits;
   p.keys_per_split = (int)kps;
   if (p.splits > 1) {
-    p.partials_bytes = (size_t)units * p.splits * 16 * (size_t)(D + 2) * 4;
-    p.workspace_bytes = p.partials_bytes;
+    // splits > 1 only when units < target_wgs <= kMaxCounters, so the
+    // counters fit their fixed area
+    p.partials_bytes = (size_t)units * p.splits * 16 * (size_t)(D + 4) * 4;
+    p.workspace_bytes = kCounterBytes + p.partials_bytes;
   }
   if (GQA_DECODE_WIDE && !paged && g > GQA_DECODE_WIDE_MIN_G) {
     // the prefill view: B * H_kv units of ceil(g / 128) row blocks, two
@@ -572,7 +623,7 @@ DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
     p.wide_splits = (int)ws;
     p.wide_kps = (int)wk;
     p.partials_bytes = ws > 1 ? (size_t)B * H * ws * (size_t)(D + 4) * 4 : 0;
-    p.workspace_bytes = p.partials_bytes;
+    p.workspace_bytes = ws > 1 ? kCounterBytes + p.partials_bytes : 0;
   }
   return p;
 }

@@ -4,6 +4,8 @@
 #include "../../include/gqa.h"
 #include "gqa_internal.h"
 
+static_assert(gqa::kCounterBytes == GQA_DECODE_COUNTER_BYTES, "counter area size");
+
 #include <limits.h>
 
 #include <initializer_list>
@@ -113,7 +115,9 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
     p.mask_bs = M;
     p.splits = plan.wide_splits;
     p.kps = plan.wide_kps;
-    p.partials = plan.workspace_bytes > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
+    p.partials = plan.workspace_bytes > 0
+                     ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes)
+                     : nullptr;
     p.in_type = (int)in_dtype;
     p.out_f32 = out_dtype == GQA_F32;
     if (gqa::launch_prefill(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
@@ -131,7 +135,10 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
   a.keys_per_split = plan.keys_per_split;
   a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
-  if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
+  if (plan.workspace_bytes > 0) {
+    a.counters = reinterpret_cast<unsigned*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes);
+  }
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
@@ -193,7 +200,10 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   a.keys_per_split = plan.keys_per_split;
   a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
-  if (plan.workspace_bytes > 0) a.partials = reinterpret_cast<float*>(workspace);
+  if (plan.workspace_bytes > 0) {
+    a.counters = reinterpret_cast<unsigned*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes);
+  }
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }

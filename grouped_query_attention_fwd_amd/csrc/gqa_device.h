@@ -23,6 +23,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -42,6 +43,38 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 // Hardware 2^x (v_exp_f32).  exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-scope (all XCDs) relaxed store: coherent across the per-XCD L2s
+// without a cache write-back or invalidation.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Raw buffer descriptor over `bytes` bytes at `base` (gfx9 descriptor
+// format word).  Accesses past `bytes` are dropped: loads return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// Cache-policy operand of a device-scope access (the sc1 bit): like st_dev,
+// coherent across the XCDs' L2s.
+constexpr int kCpolDevice = 16;
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ f32x2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolDevice));
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, kCpolDevice);
+}
+__device__ __forceinline__ void st_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, kCpolDevice);
+}
+// s_waitcnt immediate (gfx9 layout) that waits for every vector memory
+// access of the wave, loads and stores, to complete: vmcnt 0, expcnt and
+// lgkmcnt at their maximum (no wait).
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 // bf16 (stored as raw 16-bit) to fp32: the bf16 bits are the high half.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -15,7 +15,10 @@ struct DecodeArgs {
   const void* v;
   const uint8_t* mask;  // [B, 1, M] or null
   void* out;
-  float* partials;      // [units][splits][16][D + 2] fp32, or null when splits == 1
+  float* partials;      // [units][splits][16][D + 4] fp32, or null when splits == 1
+  // [units] arrival counters (splits > 1), zero between calls: the last
+  // split of a unit to finish resets its counter and merges the unit
+  unsigned* counters;
   // paged KV (block_table != null): k/v are pools [num_blocks][H_kv][block_size][D];
   // key j of sequence b lives in block block_table[b * max_blocks + j / block_size]
   // at row j % block_size, and only keys j < kv_len[b] exist.  M = max_blocks * block_size.
@@ -59,6 +62,12 @@ struct PrefillArgs {
   bool out_f32;
 };
 
+// Decode workspace layout: kCounterBytes of arrival counters (one per unit,
+// zero between calls), then the split partials.  The counter area has the
+// same place and size for every plan, so partials never land on it.
+constexpr size_t kCounterBytes = 1024;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4);
+
 // Split plan shared by the workspace query and the decode launch, so both
 // agree for the same shapes.
 struct DecodePlan {
@@ -72,7 +81,7 @@ struct DecodePlan {
   int splits;
   int keys_per_split;
   size_t partials_bytes;
-  size_t workspace_bytes;  // 0 when splits == 1
+  size_t workspace_bytes;  // kCounterBytes + partials_bytes; 0 when splits == 1
 };
 DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged);
 

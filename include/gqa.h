@@ -62,6 +62,9 @@
 extern "C" {
 #endif
 
+/* Size of the counter area at the start of a decode workspace. */
+#define GQA_DECODE_COUNTER_BYTES 1024
+
 typedef enum {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                      */
@@ -93,11 +96,19 @@ typedef enum {
  *   mask [B, 1, M] uint8 or NULL (nonzero = key visible)
  *   out  [B, H, 1, D]     out_dtype
  *   workspace: device buffer of at least gqa_decode_workspace_size(...)
- *     bytes (may be NULL when that size is 0).  It holds per-split fp32
- *     partial results between the two kernels of the call; its contents need
- *     no initialisation and are meaningless afterwards.  Two calls that may
- *     run at the same time (different streams) need two workspaces.
- * The result is deterministic: the same inputs give bit-identical outputs.
+ *     bytes (may be NULL when that size is 0).  Its first
+ *     GQA_DECODE_COUNTER_BYTES bytes are arrival counters, one per unit of
+ *     work whose keys are split over several workgroups: the last split of
+ *     a unit to finish merges the unit's fp32 partial results, which follow
+ *     the counters.  The counter area MUST be zero before the first call
+ *     (zero the buffer once after allocating it); every call, of any shape
+ *     and through either decode entry point, leaves it zero again, so one
+ *     buffer serves every later call on the same stream that fits in it.
+ *     The rest needs no initialisation.  Nonzero counters give wrong
+ *     outputs (no error is reported).  Two calls that may run at the same
+ *     time (different streams) need two workspaces.
+ * The result is deterministic: the same inputs give bit-identical outputs
+ * (the splits are always merged in split order, whichever finishes last).
  */
 gqa_status_t gqa_decode(const void* q, const void* k, const void* v,
                         const uint8_t* mask, void* out,
@@ -132,7 +143,8 @@ size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D);
  *               past the last used block are never read)
  *   out         [B, H, 1, D]                          out_dtype
  *   workspace   at least gqa_decode_paged_workspace_size(...) bytes, with
- *               the same rules as for gqa_decode
+ *               the same rules as for gqa_decode (counter area zero before
+ *               the first call, left zero by every call)
  * Key t of sequence b and KV head j is row
  *   k_pool[block_table[b][t / block_size], j, t % block_size, :].
  * A sequence with kv_len[b] == 0 sees no key and yields NaN.  The result

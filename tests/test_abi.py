@@ -159,6 +159,19 @@ def test_workspace_size_rules(lib):
     assert s2 > 0 and s2 % 4 == 0
     # a pure function of the sizes
     assert f(1, 8, 1, 65536, 128) == s2
+    # layout: the counter area, then [units][splits][16][D + 4] fp32 partials
+    # (one unit of 8 heads, 256 splits of 256 keys)
+    assert s2 == gqa.DECODE_COUNTER_BYTES + 1 * 256 * 16 * (128 + 4) * 4
+    # the large-group path (64 heads on one KV head) keeps the counter area
+    # in front of its [B*H][splits][D + 4] partials (47 splits of 64 keys)
+    assert f(1, 64, 1, 3000, 64) == gqa.DECODE_COUNTER_BYTES + 64 * 47 * (64 + 4) * 4
+
+
+def test_counter_area_constant_matches_header():
+    import re
+    with open(os.path.join(ROOT, "include", "gqa.h")) as fh:
+        m = re.search(r"#define GQA_DECODE_COUNTER_BYTES (\d+)", fh.read())
+    assert m and int(m.group(1)) == gqa.DECODE_COUNTER_BYTES
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -121,6 +121,44 @@ def test_decode_deterministic_and_workspace_reuse():
     gqa.decode(*to_dev(q2, k2, v2), workspace=ws)
     assert torch.equal(gqa.decode(qd, kd, vd, workspace=ws), outs[0])
     compare(outs[0], oracle_out(q, k, v), TOL[torch.bfloat16], "reuse")
+    torch.cuda.synchronize()
+    assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0
+
+
+def test_decode_workspace_shared_across_shapes_and_entry_points():
+    """One workspace serves decode calls of different shapes, the
+    large-group path and the paged form in turn: each call leaves the
+    counter area zero, and what lies behind it needs no initialisation
+    (it is filled with 0xFF before every call here), so every result equals
+    the one from a fresh zeroed workspace."""
+    say("workspace shared across shapes")
+    cases = [(2, 32, 8, 4096, 128, torch.bfloat16), (1, 64, 1, 3000, 64, torch.bfloat16),
+             (3, 12, 4, 777, 128, torch.float16), (2, 8, 2, 5000, 32, torch.float32),
+             (16, 32, 8, 4096, 128, torch.bfloat16)]
+    sizes = [gqa.decode_workspace_size(B, H, Hk, M, D) for B, H, Hk, M, D, _ in cases]
+    qp, kpool, vpool, table, kl = workloads.random_paged_case(53, 4, 32, 8, 128, 16, 3000,
+                                                              torch.bfloat16)
+    paged = [t.cuda() for t in (qp, kpool, vpool, table, kl)]
+    sizes.append(gqa.decode_paged_workspace_size(4, 32, 8, table.shape[1], 16, 128))
+    assert min(sizes) > 0
+    ws = torch.zeros(max(sizes), dtype=torch.uint8, device="cuda")
+    inputs = [to_dev(*workloads.random_case(60 + i, B, H, Hk, 1, M, D, dt)[:3])
+              for i, (B, H, Hk, M, D, dt) in enumerate(cases)]
+    fresh = [gqa.decode(*x, workspace=torch.zeros(n, dtype=torch.uint8, device="cuda")).clone()
+             for x, n in zip(inputs, sizes)]
+    fresh_paged = gqa.decode_paged(*paged, workspace=torch.zeros(sizes[-1], dtype=torch.uint8,
+                                                                 device="cuda")).clone()
+    nc = gqa.DECODE_COUNTER_BYTES
+    for rep in range(2):
+        for i in [4, 0, 1, 2, 3] if rep == 0 else [3, 1, 0, 4, 2]:
+            ws[nc:].fill_(0xFF)
+            assert torch.equal(gqa.decode(*inputs[i], workspace=ws), fresh[i]), (rep, i)
+            torch.cuda.synchronize()
+            assert ws[:nc].count_nonzero().item() == 0, (rep, i)
+        ws[nc:].fill_(0xFF)
+        assert torch.equal(gqa.decode_paged(*paged, workspace=ws), fresh_paged), rep
+        torch.cuda.synchronize()
+        assert ws[:nc].count_nonzero().item() == 0, rep
 
 
 def test_decode_mistral7b_full():

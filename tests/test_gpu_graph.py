@@ -1,6 +1,8 @@
 """HIP-graph capture of the prepared calls: every replay, with eager work and
 synchronisations in between, must give the eager result bit for bit (the
-kernels record no memset; the decode workspace needs no clearing)."""
+kernels record no memset: the decode workspace is zeroed once, at
+allocation, and every call, replays included, leaves its counter area
+zero)."""
 
 import sys
 
@@ -43,9 +45,10 @@ def replay_matches(op, reps=4):
 def test_graph_decode():
     say("graph decode")
     q, k, v, _ = workloads.random_case(60, 4, 32, 8, 1, 4096, 128, torch.bfloat16)
-    ws = torch.empty(gqa.decode_workspace_size(4, 32, 8, 4096, 128), dtype=torch.uint8,
+    ws = torch.zeros(gqa.decode_workspace_size(4, 32, 8, 4096, 128), dtype=torch.uint8,
                      device="cuda")
     replay_matches(gqa.decode_op(*to_dev(q, k, v), workspace=ws))
+    assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0
 
 
 def test_graph_decode_paged():
@@ -54,8 +57,9 @@ def test_graph_decode_paged():
                                                          torch.bfloat16)
     dev = [t.cuda() for t in (q, kp, vp, table, lens)]
     need = gqa.decode_paged_workspace_size(4, 32, 8, table.shape[1], 16, 128)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
     replay_matches(gqa.decode_paged_op(*dev, workspace=ws))
+    assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0
 
 
 def test_graph_prefill_and_band():

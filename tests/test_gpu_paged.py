@@ -145,10 +145,14 @@ def test_paged_determinism_and_workspace_reuse():
                                                        torch.bfloat16)
     dev = [t.cuda() for t in (q, kp, vp, table, kl)]
     need = gqa.decode_paged_workspace_size(4, 32, 8, table.shape[1], 16, 128)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     op = gqa.decode_paged_op(*dev, workspace=ws)
     a = op().clone()
-    ws.fill_(0xFF)                           # stale workspace contents do not matter
+    torch.cuda.synchronize()
+    nc = gqa.DECODE_COUNTER_BYTES
+    assert ws[:nc].count_nonzero().item() == 0   # the call leaves its counters zero
+    ws[nc:].fill_(0xFF)                          # the partials need no initialisation
     b = op().clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
