@@ -68,6 +68,14 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #endif
 static_assert(GQA_DECODE_TARGET_WGS <= kMaxCounters && GQA_DECODE_PAGED_TARGET_WGS <= kMaxCounters,
               "a split plan needs fewer units than the counter area holds");
+static_assert(GQA_DECODE_PAGED_TARGET_WGS % 8 == 0, "the XCD-grouped piece order permutes [0, G)");
+// 1: a paged decode that splits keys cuts them into pieces balanced over
+// the actual sequence lengths, planned in the kernel (GQA_DECODE_PAGED_
+// TARGET_WGS workgroups); 0: the static split plan, sized for the longest
+// possible sequence.
+#ifndef GQA_DECODE_PAGED_PIECES
+#define GQA_DECODE_PAGED_PIECES 1
+#endif
 
 template <bool H16, int DP>
 struct DecCfg {
@@ -142,9 +150,9 @@ __device__ __forceinline__ uint32_t part_row(int split, int hh, int D) {
 // QPT of them per round trip; every load of a round trip is issued before
 // any of its arithmetic.
 template <int ET, bool OUTF32, int QPT, int SB>
-__device__ __forceinline__ void merge_quads(const DecodeArgs& a, __amdgpu_buffer_rsrc_t prs, int b,
-                                            int h0, int gh, int tid) {
-  const int D = a.D, DQ = a.D >> 2, S = a.splits;
+__device__ __forceinline__ void merge_quads(const DecodeArgs& a, __amdgpu_buffer_rsrc_t prs, int S,
+                                            int b, int h0, int gh, int tid) {
+  const int D = a.D, DQ = a.D >> 2;
   const int nq = gh * DQ;
   const float sl = kLog2e / sqrtf((float)D);
   for (int q0 = tid; q0 < nq; q0 += QPT * kThreads) {
@@ -206,6 +214,87 @@ __device__ __forceinline__ void merge_quads(const DecodeArgs& a, __amdgpu_buffer
   }
 }
 
+// Where a workgroup's keys lie: unit (b, KV head, head chunk), its split s
+// of S, the index `first` of the unit's first partial, and keys
+// [k_begin, k_end).
+struct Piece {
+  int unit, s, S, first, k_begin, k_end;
+};
+
+// Length-balanced pieces of a paged batch (a.pieces > 0): at most G =
+// a.pieces workgroups, one per piece, with the longest piece as short as
+// the lengths allow.  Unit u (b, KV head, head chunk) has n_u = ceil(len_b
+// / 64) groups of 64 keys; with pieces of at most P groups it takes S_u =
+// max(1, ceil(n_u / P)) pieces, and P is the smallest value with
+// sum_u S_u <= G, found by bisection between ceil(N / G) and
+// ceil(N / (G - U)) (N = sum_u n_u, U units; the upper end always fits,
+// since sum_u S_u <= N / P + U).  Unit u's groups are then cut into S_u
+// near-equal pieces.  Pieces are numbered unit by unit, units in order;
+// workgroup i takes piece i, and workgroups past the last piece have none.
+// All units of batch row b share its length, so the sums run over batch
+// rows, fewer than 256 since U < 256, one wave reduction per 64 rows.
+// Every wave computes the plan itself; the result is wave-uniform.
+__device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int i, Piece& pc) {
+  const int lane = threadIdx.x & 63;
+  const int per_b = a.H_kv * a.head_chunks;
+  const int U = a.B * per_b;
+  const int G = a.pieces;
+  const int rounds = (a.B + 63) >> 6;  // at most 4
+  int len[4], n[4];
+  int N = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int b = lane + 64 * r;
+    len[r] = (r < rounds && b < a.B) ? min(max(a.kv_len[b], 0), a.M) : 0;
+    n[r] = (len[r] + 63) >> 6;
+    N += n[r];
+  }
+  N = wave_sum(N) * per_b;  // the host keeps U * ceil(M / 64) below 2^30
+  auto pieces_for = [&](int P) {
+    int t = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < rounds && lane + 64 * r < a.B)
+        t += max(1u, ((unsigned)n[r] + (unsigned)P - 1u) / (unsigned)P);
+    return wave_sum(t) * per_b;
+  };
+  int lo = max(1, (N + G - 1) / G);
+  int hi = max(lo, (N + (G - U) - 1) / (G - U));
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pieces_for(mid) <= G) hi = mid; else lo = mid + 1;
+  }
+  const int P = lo;
+  int carry = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int b = lane + 64 * r;
+    const int sb = (b < a.B) ? max(1u, ((unsigned)n[r] + (unsigned)P - 1u) / (unsigned)P) : 0;
+    int incl = wave_incl_scan(sb * per_b) + carry;
+    const int excl = incl - sb * per_b;
+    const unsigned long long hit = __ballot(b < a.B && excl <= i && i < incl);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int S = __shfl(sb, src, 64);
+      const int e0 = __shfl(excl, src, 64);
+      const int nb = __shfl(n[r], src, 64);
+      const int blen = __shfl(len[r], src, 64);
+      const int local = i - e0;
+      const int ju = local / S;
+      pc.unit = (64 * r + src) * per_b + ju;
+      pc.s = local - ju * S;
+      pc.S = S;
+      pc.first = e0 + ju * S;
+      if (pc.first + S > G) return false;  // never: the plan fits G (keeps partials in bounds)
+      // near-equal cut of the unit's nb groups into S pieces
+      pc.k_begin = min(64 * (int)(((long long)pc.s * nb) / S), blen);
+      pc.k_end = min(64 * (int)(((long long)(pc.s + 1) * nb) / S), blen);
+      return true;
+    }
+    carry = __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
 // EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is
 // given.  PAGED: K/V rows are found through a block table and each sequence
 // has its own length.
@@ -226,12 +315,28 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   // workgroups are renumbered so that the head chunks of one (b, KV head),
   // which stream the same K/V rows, run side by side on one XCD (workgroup
   // L goes to XCD L % 8), where the later reader can find rows in L2.
-  int unit = blockIdx.x;
-  const int s = blockIdx.y;
-  if (a.xcd_group) {
-    const int x = unit & 7, i = unit >> 3;
-    unit = ((i / a.head_chunks) * 8 + x) * a.head_chunks + i % a.head_chunks;
+  Piece pc;
+  if (PAGED && a.pieces > 0) {
+    // XCD-grouped piece order: workgroup L runs on XCD L % 8 and takes piece
+    // (L % 8) * G/8 + L / 8, so each XCD walks a run of consecutive pieces
+    // (whole units, whose head chunks read the same K/V rows, stay on one L2)
+    const int L = blockIdx.x;
+    if (!paged_piece(a, (L & 7) * (a.pieces >> 3) + (L >> 3), pc)) return;  // uniform
+  } else {
+    pc.unit = blockIdx.x;
+    if (a.xcd_group) {
+      const int x = pc.unit & 7, i = pc.unit >> 3;
+      pc.unit = ((i / a.head_chunks) * 8 + x) * a.head_chunks + i % a.head_chunks;
+    }
+    pc.s = blockIdx.y;
+    pc.S = a.splits;
+    pc.first = pc.unit * a.splits;
+    pc.k_begin = pc.s * a.keys_per_split;
+    pc.k_end = min(a.M, pc.k_begin + a.keys_per_split);
   }
+  const int unit = __builtin_amdgcn_readfirstlane(pc.unit);
+  const int s = __builtin_amdgcn_readfirstlane(pc.s);
+  const int S = __builtin_amdgcn_readfirstlane(pc.S);
   const int per_b = a.H_kv * a.head_chunks;
   const int b = unit / per_b;
   const int rem = unit - b * per_b;
@@ -242,8 +347,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   const int D = EXACT ? DP : a.D;
   const int M = a.M;
 
-  const int k_begin = s * a.keys_per_split;
-  int k_end = min(M, k_begin + a.keys_per_split);
+  const int k_begin = __builtin_amdgcn_readfirstlane(pc.k_begin);
+  int k_end = __builtin_amdgcn_readfirstlane(pc.k_end);
   if constexpr (PAGED) k_end = min(k_end, max(0, a.kv_len[b]));   // this sequence's keys
 
   // K/V rows are addressed per aligned group of 16 keys.  `group_off(g16)`
@@ -487,10 +592,10 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   // Each thread combines the four waves for quads (head, 4 consecutive d).
   const int DQ = D >> 2;  // D % 4 == 0 for every supported type
   const int nq = gh * DQ;
-  const bool single = (a.splits == 1);
+  const bool single = (S == 1);
   const __amdgpu_buffer_rsrc_t prs = raw_rsrc(
-      single ? a.out : a.partials + (size_t)unit * a.splits * 16 * (D + 4),
-      single ? 0u : part_row(a.splits, 0, D));
+      single ? a.out : a.partials + (size_t)__builtin_amdgcn_readfirstlane(pc.first) * 16 * (D + 4),
+      single ? 0u : part_row(S, 0, D));
   for (int q = tid; q < nq; q += kThreads) {
     const int hh = q / DQ;
     const int d = 4 * (q - hh * DQ);
@@ -530,24 +635,24 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   if (tid == 0) {
     const unsigned t = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (t == (unsigned)a.splits - 1u);
+    s_last = (t == (unsigned)S - 1u);
   }
   __syncthreads();
   if (!s_last) return;
   if (tid == 0) st_dev(a.counters + unit, 0u);  // ready for the next call
-  if (a.splits <= 2) {
-    merge_quads<ET, OUTF32, 4, 2>(a, prs, b, h0, gh, tid);
-  } else if (a.splits <= 4) {
-    merge_quads<ET, OUTF32, 2, 4>(a, prs, b, h0, gh, tid);
+  if (S <= 2) {
+    merge_quads<ET, OUTF32, 4, 2>(a, prs, S, b, h0, gh, tid);
+  } else if (S <= 4) {
+    merge_quads<ET, OUTF32, 2, 4>(a, prs, S, b, h0, gh, tid);
   } else {
-    merge_quads<ET, OUTF32, 1, 8>(a, prs, b, h0, gh, tid);
+    merge_quads<ET, OUTF32, 1, 8>(a, prs, S, b, h0, gh, tid);
   }
 }
 
 template <int ET, int DP, bool EXACT, bool OUTF32>
 hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * a.head_chunks;
-  const dim3 grid(units, a.splits);
+  const dim3 grid = a.pieces > 0 ? dim3(a.pieces) : dim3(units, a.splits);
   if (a.block_table) {  // the paged form takes no mask
     hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else if (a.mask) {
@@ -606,6 +711,15 @@ DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
     // counters fit their fixed area
     p.partials_bytes = (size_t)units * p.splits * 16 * (size_t)(D + 4) * 4;
     p.workspace_bytes = kCounterBytes + p.partials_bytes;
+    const long groups = units * ((M + 63) / 64);  // 64-key groups of the longest batch
+    if (paged && GQA_DECODE_PAGED_PIECES && groups < (1L << 30)) {
+      // length-balanced pieces planned on the device (in int arithmetic,
+      // hence the bound on the group count), one workgroup per piece
+      p.pieces = (int)target_wgs;
+      p.xcd_group = 0;
+      p.partials_bytes = (size_t)p.pieces * 16 * (size_t)(D + 4) * 4;
+      p.workspace_bytes = kCounterBytes + p.partials_bytes;
+    }
   }
   if (GQA_DECODE_WIDE && !paged && g > GQA_DECODE_WIDE_MIN_G) {
     // the prefill view: B * H_kv units of ceil(g / 128) row blocks, two

@@ -198,6 +198,7 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
   a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
+  a.pieces = plan.pieces;
   a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (plan.workspace_bytes > 0) {

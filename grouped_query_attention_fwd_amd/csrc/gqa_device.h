@@ -198,6 +198,32 @@ __device__ __forceinline__ float rows_max(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Sum of an int over the 64 lanes of a wave, in every lane: DPP adds inside
+// each 16-lane row (quad swaps, then the half-row and row mirrors), then the
+// two row swaps.  Every lane must be active.
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = (int)(a[0] + a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)(b[0] + b[1]);
+}
+// Inclusive prefix sum of an int over the 64 lanes of a wave: DPP row
+// shifts by 1, 2, 4 and 8 inside each 16-lane row (lanes shifted in from
+// outside the row add zero), then lane 15 of each row is added to the next
+// row and lane 31 to the upper half.  Every lane must be active.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
 __device__ __forceinline__ float rows_sum(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);

@@ -32,6 +32,9 @@ struct DecodeArgs {
   int xcd_group;        // 1: the head chunks of one (b, KV head) share an XCD
   int splits;           // key-range splits per unit
   int keys_per_split;   // multiple of 256
+  // paged only: > 0 launches this many workgroups, which split the keys in
+  // pieces balanced over the actual lengths (planned in the kernel)
+  int pieces;
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };
@@ -80,6 +83,7 @@ struct DecodePlan {
   int xcd_group;
   int splits;
   int keys_per_split;
+  int pieces;              // paged: length-balanced pieces (0: static splits)
   size_t partials_bytes;
   size_t workspace_bytes;  // kCounterBytes + partials_bytes; 0 when splits == 1
 };
