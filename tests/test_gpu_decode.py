@@ -55,6 +55,10 @@ SMALL = [
     (42, 1, 4, 1, 300, 256, torch.float16, None),
     (43, 2, 6, 3, 130, 24, torch.float16, "random"),
     (44, 4, 8, 2, 4097, 96, torch.float16, None),
+    # one long sequence: 4 units of 64 key splits each, merged eight splits
+    # per round trip
+    (45, 1, 16, 4, 65536, 128, torch.bfloat16, None),
+    (46, 1, 8, 1, 40000, 64, torch.float32, "padding"),   # 1 unit, 157 splits
 ]
 
 
