@@ -12,7 +12,9 @@
 // used for all the query heads of its group (up to 16 per workgroup).
 //
 // Work split: one workgroup of four waves per (batch row, KV head, chunk of
-// up to 16 query heads, key range "split").  Inside a workgroup the waves
+// up to 16 query heads, key range).  The key ranges are equal splits, or,
+// for a paged batch, pieces balanced over the sequences' actual lengths,
+// planned by every workgroup from kv_len.  Inside a workgroup the waves
 // take interleaved chunks of KC keys, addressed per aligned group of 16 keys
 // (contiguous rows, or one block-table entry of a paged cache, in which case
 // each sequence's own length ends its key range).  Per chunk a wave
@@ -31,8 +33,8 @@
 // written directly.  Otherwise every workgroup stores its (m, l, acc) partial
 // to the fp32 workspace and takes a ticket from the unit's arrival counter;
 // the workgroup that arrives last merges the unit's splits in split order
-// (so the result is bit-reproducible whichever finishes last), then sets the
-// partials and the counter back to zero.
+// (so the result is bit-reproducible whichever finishes last) and sets the
+// counter back to zero for the next call.
 // Groups of more than 32 heads (contiguous cache) go through the prefill
 // kernel instead, with the heads as query rows (see plan_decode).
 #include "gqa_device.h"
