@@ -168,8 +168,9 @@ def make_call(info, torch):
 
 def time_workload(info, steps, warmup, torch):
     """Eager timing on the launch stream: HIP events around K back-to-back
-    steps (throughput), then around every step of a second pass (per-launch
-    duration)."""
+    steps (throughput and the average launch duration), then around every
+    step of a second pass (the per-call spread, which also carries the
+    events' own packets)."""
     call = make_call(info, torch)
     # warm-up: at least `warmup` steps and at least WARMUP_S seconds of work,
     # so the GPU clocks have settled before the timed region
@@ -260,7 +261,10 @@ def traffic_for(kind, workload, launch_units):
 def result_for(info, timing):
     w = info["w"]
     kind = info["kind"]
-    avg_s = timing["launch_ms_avg"] * 1e-3
+    # average launch duration: two HIP events around K back-to-back launches
+    # on the launching stream, divided by K (an event pair around every
+    # single call, reported as launch_us, adds the events' own packets)
+    avg_s = timing["ms_per_step"] * 1e-3
     whole_s = timing["ms_per_step"] * 1e-3
     if kind in ("decode", "decode_paged"):
         achieved = info["units"] / avg_s / 1e9
@@ -288,7 +292,7 @@ def result_for(info, timing):
         if w.band is not None:
             config["band"] = {"q_offset": w.q_offset, "window_left": w.window_left,
                               "window_right": w.window_right}
-    roof["duration_us"] = round(timing["launch_ms_avg"] * 1e3, 2)
+    roof["duration_us"] = round(timing["ms_per_step"] * 1e3, 2)
     return {
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
         "ms_per_step": round(timing["ms_per_step"], 5),
@@ -452,7 +456,8 @@ def main():
         results[name] = result_for(info, timing)
         results[name]["steps"] = steps
         log(f"[bench] {name}: {results[name]['value']} {results[name]['unit']} "
-            f"(launch avg {results[name]['launch_us']['avg']} us)")
+            f"({results[name]['roofline']['duration_us']} us per launch; with an event pair "
+            f"around each call {results[name]['launch_us']['avg']} us)")
         if name == primary:
             primary_info = info
         else:
@@ -473,7 +478,7 @@ def main():
             timing = time_workload(info, max(10, args.steps // 2), args.warmup, torch)
             r = result_for(info, timing)
             sweep.append({"g": w.H // w.H_kv, "H_kv": w.H_kv, "value": r["value"],
-                          "unit": r["unit"], "launch_us": r["launch_us"]["avg"],
+                          "unit": r["unit"], "us_per_launch": r["roofline"]["duration_us"],
                           "frac": r["roofline"]["frac"], "kv_bytes": kv})
             del info
             torch.cuda.empty_cache()
