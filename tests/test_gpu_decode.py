@@ -129,6 +129,46 @@ def test_decode_deterministic_and_workspace_reuse():
     assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0
 
 
+def test_decode_one_shot_calls_on_two_streams():
+    """decode() without a workspace keeps one zeroed buffer per stream:
+    calls queued on two streams at once use different buffers and both give
+    the result of a call with a fresh workspace; a larger call on the same
+    stream then replaces that stream's buffer."""
+    say("one-shot decode on two streams")
+    B, H, H_kv, M, D = 4, 32, 8, 4096, 128
+    ins = [to_dev(*workloads.random_case(70 + i, B, H, H_kv, 1, M, D, torch.bfloat16)[:3])
+           for i in range(2)]
+    want = [gqa.decode(*x, workspace=torch.zeros(gqa.decode_workspace_size(B, H, H_kv, M, D),
+                                                 dtype=torch.uint8, device="cuda")).clone()
+            for x in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                outs[i].append(gqa.decode(*ins[i]))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for o in outs[i]:
+            assert torch.equal(o, want[i]), i
+    # a call with more partials (100 units x 3 splits) grows the first
+    # stream's buffer; results stay exact
+    n_big = gqa.decode_workspace_size(25, 16, 4, 4096, D)
+    assert n_big > gqa.decode_workspace_size(B, H, H_kv, M, D)
+    q3, k3, v3 = to_dev(*workloads.random_case(72, 25, 16, 4, 1, 4096, D, torch.bfloat16)[:3])
+    big = gqa.decode(q3, k3, v3, workspace=torch.zeros(n_big, dtype=torch.uint8,
+                                                       device="cuda")).clone()
+    with torch.cuda.stream(streams[0]):
+        got_big = gqa.decode(q3, k3, v3)
+        got_small = gqa.decode(*ins[0])
+    torch.cuda.synchronize()
+    assert torch.equal(got_big, big)
+    assert torch.equal(got_small, want[0])
+
+
 def test_decode_workspace_shared_across_shapes_and_entry_points():
     """One workspace serves decode calls of different shapes, the
     large-group path and the paged form in turn: each call leaves the
