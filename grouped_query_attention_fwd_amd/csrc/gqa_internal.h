@@ -15,7 +15,9 @@ struct DecodeArgs {
   const void* v;
   const uint8_t* mask;  // [B, 1, M] or null
   void* out;
-  float* partials;      // [units][splits][16][D + 4] fp32, or null when splits == 1
+  // [units][splits][16][D + 4] fp32 (with paged pieces: [pieces][16][D + 4],
+  // a unit's pieces consecutive), or null when splits == 1
+  float* partials;
   // [units] arrival counters (splits > 1), zero between calls: the last
   // split of a unit to finish resets its counter and merges the unit
   unsigned* counters;
