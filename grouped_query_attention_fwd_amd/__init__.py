@@ -39,7 +39,7 @@ __all__ = ["decode", "decode_paged", "prefill", "prefill_band", "decode_op", "de
 
 # Bytes of arrival counters at the start of a decode workspace; they must be
 # zero before the first call, and every call leaves them zero.
-DECODE_COUNTER_BYTES = 1024
+DECODE_COUNTER_BYTES = 16384
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")

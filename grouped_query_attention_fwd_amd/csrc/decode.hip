@@ -70,7 +70,7 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #endif
 static_assert(GQA_DECODE_TARGET_WGS <= kMaxCounters && GQA_DECODE_PAGED_TARGET_WGS <= kMaxCounters,
               "a split plan needs fewer units than the counter area holds");
-static_assert(GQA_DECODE_PAGED_TARGET_WGS % 8 == 0, "the XCD-grouped piece order permutes [0, G)");
+static_assert(GQA_DECODE_PAGED_TARGET_WGS % 8 == 0, "the piece grid is a multiple of the XCD count");
 // 1: a paged decode that splits keys cuts them into pieces balanced over
 // the actual sequence lengths, planned in the kernel (GQA_DECODE_PAGED_
 // TARGET_WGS workgroups); 0: the static split plan, sized for the longest
@@ -231,46 +231,63 @@ struct Piece {
 // sum_u S_u <= G, found by bisection between ceil(N / G) and
 // ceil(N / (G - U)) (N = sum_u n_u, U units; the upper end always fits,
 // since sum_u S_u <= N / P + U).  Unit u's groups are then cut into S_u
-// near-equal pieces.  Pieces are numbered unit by unit, units in order;
-// workgroup i takes piece i, and workgroups past the last piece have none.
+// near-equal pieces; with 256 units or more and near-equal lengths, each
+// unit is one piece instead.  Pieces are numbered unit by unit, units in
+// order, and spread over the XCDs (below); workgroups left over have none.
 // All units of batch row b share its length, so the sums run over batch
-// rows, fewer than 256 since U < 256, one wave reduction per 64 rows.
-// Every wave computes the plan itself; the result is wave-uniform.
-__device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int i, Piece& pc) {
+// rows, one wave reduction per 64 rows (kv_len is re-read from cache in
+// each pass).  Every wave computes the plan itself; the result is
+// wave-uniform.
+__device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& pc) {
   const int lane = threadIdx.x & 63;
   const int per_b = a.H_kv * a.head_chunks;
   const int U = a.B * per_b;
   const int G = a.pieces;
-  const int rounds = (a.B + 63) >> 6;  // at most 4
-  int len[4], n[4];
-  int N = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int b = lane + 64 * r;
-    len[r] = (r < rounds && b < a.B) ? min(max(a.kv_len[b], 0), a.M) : 0;
-    n[r] = (len[r] + 63) >> 6;
-    N += n[r];
+  const int rounds = (a.B + 63) >> 6;
+  // clamped length and 64-key groups of batch row b (0 past the last row)
+  auto len_of = [&](int b) { return b < a.B ? min(max(a.kv_len[b], 0), a.M) : 0; };
+  int N = 0, nmax = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int n = (len_of(lane + 64 * r) + 63) >> 6;
+    N += n;
+    nmax = max(nmax, n);
   }
   N = wave_sum(N) * per_b;  // the host keeps U * ceil(M / 64) below 2^30
+  nmax = wave_max(nmax);
+  auto pieces_of = [&](int b, int P) {
+    const unsigned n = (unsigned)(len_of(b) + 63) >> 6;
+    return b < a.B ? (int)max(1u, (n + (unsigned)P - 1u) / (unsigned)P) : 0;
+  };
   auto pieces_for = [&](int P) {
     int t = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (r < rounds && lane + 64 * r < a.B)
-        t += max(1u, ((unsigned)n[r] + (unsigned)P - 1u) / (unsigned)P);
+    for (int r = 0; r < rounds; ++r) t += pieces_of(lane + 64 * r, P);
     return wave_sum(t) * per_b;
   };
   int lo = max(1, (N + G - 1) / G);
   int hi = max(lo, (N + (G - U) - 1) / (G - U));
+  // With more units than one wave of workgroups and near-equal lengths
+  // (longest within 25 % of the mean), one piece per unit: cutting them
+  // would only add a second round of workgroups and merges.
+  if (U >= 256 && 4LL * nmax * U <= 5LL * N) lo = hi = max(nmax, 1);
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (pieces_for(mid) <= G) hi = mid; else lo = mid + 1;
   }
   const int P = lo;
+  // XCD-grouped order over the T pieces of the plan: workgroup L runs on XCD
+  // L % 8 and takes piece (L % 8) * ceil(T / 8) + L / 8, so each XCD walks a
+  // run of consecutive pieces (whole units, whose head chunks read the same
+  // K/V rows, stay on one L2) and the XCDs get equal shares; workgroups past
+  // an XCD's share have none.
+  const int T = pieces_for(P);
+  const int per = (T + 7) >> 3;
+  if ((L >> 3) >= per) return false;
+  const int i = (L & 7) * per + (L >> 3);
+  if (i >= T) return false;
   int carry = 0;
   for (int r = 0; r < rounds; ++r) {
     const int b = lane + 64 * r;
-    const int sb = (b < a.B) ? max(1u, ((unsigned)n[r] + (unsigned)P - 1u) / (unsigned)P) : 0;
+    const int sb = pieces_of(b, P);
     int incl = wave_incl_scan(sb * per_b) + carry;
     const int excl = incl - sb * per_b;
     const unsigned long long hit = __ballot(b < a.B && excl <= i && i < incl);
@@ -278,8 +295,8 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int i, Piece& p
       const int src = __builtin_ctzll(hit);
       const int S = __shfl(sb, src, 64);
       const int e0 = __shfl(excl, src, 64);
-      const int nb = __shfl(n[r], src, 64);
-      const int blen = __shfl(len[r], src, 64);
+      const int blen = len_of(64 * r + src);
+      const int nb = (blen + 63) >> 6;
       const int local = i - e0;
       const int ju = local / S;
       pc.unit = (64 * r + src) * per_b + ju;
@@ -319,11 +336,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   // L goes to XCD L % 8), where the later reader can find rows in L2.
   Piece pc;
   if (PAGED && a.pieces > 0) {
-    // XCD-grouped piece order: workgroup L runs on XCD L % 8 and takes piece
-    // (L % 8) * G/8 + L / 8, so each XCD walks a run of consecutive pieces
-    // (whole units, whose head chunks read the same K/V rows, stay on one L2)
-    const int L = blockIdx.x;
-    if (!paged_piece(a, (L & 7) * (a.pieces >> 3) + (L >> 3), pc)) return;  // uniform
+    if (!paged_piece(a, blockIdx.x, pc)) return;  // uniform: no piece for this workgroup
   } else {
     pc.unit = blockIdx.x;
     if (a.xcd_group) {
@@ -454,13 +467,29 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     return ch;
   };
 
+  // The workgroup walks its keys in rounds of kstride, wave w taking chunk w
+  // of each round.  With a.rotate the walk starts at a round that depends
+  // on the unit and split and wraps around, so concurrent workgroups whose
+  // ranges start at equally aligned addresses (caches of 8 MB or more per
+  // KV head) are not at the same low address bits at the same time; the
+  // order is fixed per workgroup, so results stay reproducible.
   const int kstride = kWaves * C::KC;
-  int base = k_begin + w * C::KC;
+  const int nround = (k_end - k_begin + kstride - 1) / kstride;
+  const int r0 = (a.rotate && nround > 0)
+                     ? (int)(((unsigned)unit * 37u + (unsigned)s * 7u) % (unsigned)nround)
+                     : 0;
+  auto base_of = [&](int t) {
+    int r = t + r0;
+    if (r >= nround) r -= nround;
+    return k_begin + r * kstride + w * C::KC;
+  };
+  int t_round = 0;
+  int base = base_of(0);
   Chunk cur;
-  if (base < k_end) cur = load_chunk(base);
-  while (base < k_end) {
-    const int nb = base + kstride;
-    const bool more = nb < k_end;
+  if (nround > 0) cur = load_chunk(base);
+  while (t_round < nround) {
+    const bool more = t_round + 1 < nround;
+    const int nb = more ? base_of(t_round + 1) : base;
     Chunk nxt;
     if constexpr (C::PREFETCH) {
       if (more) nxt = load_chunk(nb);
@@ -572,6 +601,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       cur = load_chunk(nb);
     }
     base = nb;
+    ++t_round;
   }
 
   // ---- merge the waves through LDS -----------------------------------
@@ -713,15 +743,19 @@ DecodePlan plan_decode(int B, int H, int H_kv, int M, int D, bool paged) {
     // counters fit their fixed area
     p.partials_bytes = (size_t)units * p.splits * 16 * (size_t)(D + 4) * 4;
     p.workspace_bytes = kCounterBytes + p.partials_bytes;
-    const long groups = units * ((M + 63) / 64);  // 64-key groups of the longest batch
-    if (paged && GQA_DECODE_PAGED_PIECES && groups < (1L << 30)) {
-      // length-balanced pieces planned on the device (in int arithmetic,
-      // hence the bound on the group count), one workgroup per piece
-      p.pieces = (int)target_wgs;
-      p.xcd_group = 0;
-      p.partials_bytes = (size_t)p.pieces * 16 * (size_t)(D + 4) * 4;
-      p.workspace_bytes = kCounterBytes + p.partials_bytes;
-    }
+  }
+  const long groups = units * ((M + 63) / 64);  // 64-key groups of the longest batch
+  if (paged && GQA_DECODE_PAGED_PIECES && max_splits > 1 && units < kMaxCounters &&
+      groups < (1L << 30)) {
+    // length-balanced pieces planned on the device (in int arithmetic, hence
+    // the bound on the group count), one workgroup per piece: one wave of
+    // workgroups for few units, two workgroups per unit for many, a
+    // multiple of 8 for the XCD-grouped order
+    const long G = units < target_wgs ? target_wgs : (2 * units + 7) / 8 * 8;
+    p.pieces = (int)G;
+    p.xcd_group = 0;
+    p.partials_bytes = (size_t)p.pieces * 16 * (size_t)(D + 4) * 4;
+    p.workspace_bytes = kCounterBytes + p.partials_bytes;
   }
   if (GQA_DECODE_WIDE && !paged && g > GQA_DECODE_WIDE_MIN_G) {
     // the prefill view: B * H_kv units of ceil(g / 128) row blocks, two

@@ -133,6 +133,10 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
   a.xcd_group = plan.xcd_group;
   a.splits = plan.splits;
   a.keys_per_split = plan.keys_per_split;
+  // a rotated key walk measured 4-7 % faster for caches of 8 MB or more per
+  // KV head (all split ranges then start at equally aligned addresses) and
+  // about 1 % slower for smaller ones
+  a.rotate = (size_t)M * D * dtype_size(in_dtype) >= ((size_t)8 << 20) ? 1 : 0;
   a.in_type = (int)in_dtype;  // gqa_dtype_t values match kF32 / kBF16 / kF16
   a.out_f32 = out_dtype == GQA_F32;
   if (plan.workspace_bytes > 0) {

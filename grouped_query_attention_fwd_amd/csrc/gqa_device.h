@@ -211,6 +211,18 @@ __device__ __forceinline__ int wave_sum(int x) {
   auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
   return (int)(b[0] + b[1]);
 }
+// Maximum of an int over the 64 lanes of a wave, in every lane (the same
+// steps as wave_sum).
+__device__ __forceinline__ int wave_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = max((int)a[0], (int)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)b[0], (int)b[1]);
+}
 // Inclusive prefix sum of an int over the 64 lanes of a wave: DPP row
 // shifts by 1, 2, 4 and 8 inside each 16-lane row (lanes shifted in from
 // outside the row add zero), then lane 15 of each row is added to the next

@@ -37,6 +37,7 @@ struct DecodeArgs {
   // paged only: > 0 launches this many workgroups, which split the keys in
   // pieces balanced over the actual lengths (planned in the kernel)
   int pieces;
+  int rotate;           // 1: each workgroup starts its key walk at its own round
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };
@@ -70,7 +71,7 @@ struct PrefillArgs {
 // Decode workspace layout: kCounterBytes of arrival counters (one per unit,
 // zero between calls), then the split partials.  The counter area has the
 // same place and size for every plan, so partials never land on it.
-constexpr size_t kCounterBytes = 1024;
+constexpr size_t kCounterBytes = 16384;
 constexpr int kMaxCounters = (int)(kCounterBytes / 4);
 
 // Split plan shared by the workspace query and the decode launch, so both

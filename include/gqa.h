@@ -63,7 +63,7 @@ extern "C" {
 #endif
 
 /* Size of the counter area at the start of a decode workspace. */
-#define GQA_DECODE_COUNTER_BYTES 1024
+#define GQA_DECODE_COUNTER_BYTES 16384
 
 typedef enum {
   GQA_OK = 0,
@@ -150,10 +150,11 @@ size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D);
  * A sequence with kv_len[b] == 0 sees no key and yields NaN.  The result
  * equals gqa_decode over the gathered cache [B, H_kv, max_blocks*block_size,
  * D] with mask[b][0][t] = (t < kv_len[b]).
- * Work split: when the batch has fewer than 256 (batch row, KV head, head
- * chunk) units, each unit's keys are cut into pieces balanced over the
- * actual lengths (planned on the device from kv_len), merged in piece order.
- * Results are deterministic for given lengths.
+ * Work split: when the batch has fewer than 4096 (batch row, KV head, head
+ * chunk) units and more than 256 cached key slots, each unit's keys are cut
+ * into pieces balanced over the actual lengths (planned on the device from
+ * kv_len), merged in piece order.  Results are deterministic for given
+ * lengths.
  * Supported: block_size a positive multiple of 16 (else
  * GQA_ERR_UNSUPPORTED); the limits of gqa_decode with M = max_blocks *
  * block_size; block_table and kv_len are device memory, 4-byte aligned.
