@@ -329,19 +329,38 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) sc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) {
+    if constexpr (H16 && DIRECT) {
+      // D-chunk outermost: each step reads one K chunk per key block and
+      // issues NKB * QB independent MFMAs, so no accumulator chain waits on
+      // its own previous MFMA (measured 1 % faster than key block outermost;
+      // the staged-copy kernels keep the other order, which needs fewer
+      // registers)
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
-        const u32x4 kop = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * u + qg));
+        u32x4 kop[C::NKB];
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) {
-          if constexpr (H16) {
-            sc[qb][kb] = mma16<ET>(kop, qop[qb][u], sc[qb][kb]);
-          } else {
+        for (int kb = 0; kb < C::NKB; ++kb)
+          kop[kb] = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * u + qg));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sc[qb][kb] = mfma_f32(__uint_as_float(kop[e]), __uint_as_float(qop[qb][u][e]), sc[qb][kb]);
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) sc[qb][kb] = mma16<ET>(kop[kb], qop[qb][u], sc[qb][kb]);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int u = 0; u < C::QCH; ++u) {
+          const u32x4 kop = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * u + qg));
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) {
+            if constexpr (H16) {
+              sc[qb][kb] = mma16<ET>(kop, qop[qb][u], sc[qb][kb]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sc[qb][kb] = mfma_f32(__uint_as_float(kop[e]), __uint_as_float(qop[qb][u][e]), sc[qb][kb]);
+            }
           }
         }
       }
