@@ -63,6 +63,10 @@ BALANCED = [
     (34, 4, 16, 4, 128, 16, 900, torch.bfloat16, [0, 0, 0, 0]),  # no keys anywhere: NaN
     (35, 5, 20, 5, 128, 64, 3000, torch.float16, [3000, 64, 65, 2999, 128]),
     (36, 2, 8, 2, 32, 16, 6000, torch.float32, [6000, 17]),     # fp32, many pieces
+    # 320 units (more than one wave of workgroups): 640 workgroups
+    (37, 40, 16, 8, 64, 16, 700, torch.bfloat16, "uniform"),   # uneven: balanced pieces
+    (38, 40, 16, 8, 64, 16, 700, torch.bfloat16, "full"),      # even: one piece per unit
+    (39, 36, 16, 8, 64, 32, 1000, torch.float16, [1000] * 35 + [3]),  # near-even but one short
 ]
 
 
