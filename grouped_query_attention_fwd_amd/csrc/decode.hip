@@ -231,8 +231,8 @@ struct Piece {
 // sum_u S_u <= G, found by bisection between ceil(N / G) and
 // ceil(N / (G - U)) (N = sum_u n_u, U units; the upper end always fits,
 // since sum_u S_u <= N / P + U).  Unit u's groups are then cut into S_u
-// near-equal pieces; with 256 units or more and near-equal lengths, each
-// unit is one piece instead.  Pieces are numbered unit by unit, units in
+// near-equal pieces.  Near-equal lengths skip the search: each unit is one
+// piece (256 units or more) or floor(G / U) pieces.  Pieces are numbered unit by unit, units in
 // order, and spread over the XCDs (below); workgroups left over have none.
 // All units of batch row b share its length, so the sums run over batch
 // rows, one wave reduction per 64 rows (kv_len is re-read from cache in
@@ -265,10 +265,15 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
   };
   int lo = max(1, (N + G - 1) / G);
   int hi = max(lo, (N + (G - U) - 1) / (G - U));
-  // With more units than one wave of workgroups and near-equal lengths
-  // (longest within 25 % of the mean), one piece per unit: cutting them
-  // would only add a second round of workgroups and merges.
-  if (U >= 256 && 4LL * nmax * U <= 5LL * N) lo = hi = max(nmax, 1);
+  // Near-equal lengths (longest within 25 % of the mean) need no search.
+  // With more units than one wave of workgroups, one piece per unit:
+  // cutting them would only add a second round of workgroups and merges.
+  // Otherwise floor(G / U) pieces per unit, P = ceil(nmax / that), which
+  // fits G and is the search's answer when all lengths are equal.
+  if (4LL * nmax * U <= 5LL * N) {
+    const int k = U >= 256 ? 1 : G / U;
+    lo = hi = max(1, (nmax + k - 1) / k);
+  }
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (pieces_for(mid) <= G) hi = mid; else lo = mid + 1;
