@@ -241,12 +241,15 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     }
   }
 
-  float m_run[C::QB], l_run[C::QB];
+  // nmsl = -m_run * sl, the exponent offset of the weights (0 while the
+  // row has seen no visible key); it changes only with the reference.
+  float m_run[C::QB], l_run[C::QB], nmsl[C::QB];
   f32x4 acc[C::QB][C::NDB];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     m_run[qb] = kNegInf;
     l_run[qb] = 0.f;
+    nmsl[qb] = 0.f;
 #pragma unroll
     for (int i = 0; i < C::NDB; ++i) acc[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -275,6 +278,28 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // ---- tile copies -----------------------------------------------------------
   u32x4 stage[DIRECT ? 1 : C::PPT];
   // DIRECT copies: global -> LDS, no registers.  which = 0: K, 1: V.
+  // A tile that lies wholly inside the keys needs no clamping: its source is
+  // a buffer descriptor over this (b, KV head)'s rows, a wave-uniform row
+  // offset (scalar register) and a per-lane offset that does not change from
+  // tile to tile (the swizzle depends only on the row's low bits, which the
+  // advance of kWaves * RPI rows per instruction leaves alone for D <= 128),
+  // so such a copy costs no vector instructions.  Slabs of 2 GB or more take
+  // the clamped path below.
+  constexpr bool kDmaInvariant = DIRECT && ((kWaves * C::RPI) % (C::KSWZ + 1) == 0) &&
+                                 ((kWaves * C::RPI) % (C::VSWZ + 1) == 0);
+  const bool dma_buf = kDmaInvariant && (long long)M * C::ROWB <= 0x7fffffffLL;
+  uint32_t dma_off[2] = {0u, 0u};
+  __amdgpu_buffer_rsrc_t dma_rsrc[2];
+  if constexpr (kDmaInvariant) {
+    const int lrow = lane / C::CPR;
+    const int slot = lane - lrow * C::CPR;
+    const int row0 = w * C::RPI + lrow;
+    dma_off[0] = (uint32_t)(row0 * C::ROWB + ((slot ^ (row0 & C::KSWZ)) << 4));
+    dma_off[1] = (uint32_t)(row0 * C::ROWB + ((slot ^ (2 * (row0 & C::VSWZ))) << 4));
+    const uint32_t slab = dma_buf ? (uint32_t)M * C::ROWB : 0u;
+    dma_rsrc[0] = raw_rsrc(kp, slab);
+    dma_rsrc[1] = raw_rsrc(vp, slab);
+  }
   auto dma_half = [&](int t, lds_char* dst_tile, int which) {
     const int k0 = t * C::BN;
     const char* src = which ? vp : kp;
@@ -289,6 +314,26 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       const int chunk = which ? (slot ^ (2 * (row & C::VSWZ))) : (slot ^ (row & C::KSWZ));
       dma16(src + ((size_t)key * DP + chunk * 8) * 2, dst_tile + (i * kWaves + w) * 1024);
     }
+  };
+  auto dma_tile = [&](int t, lds_char* kdst, lds_char* vdst) {
+    const int k0 = t * C::BN;
+    if constexpr (kDmaInvariant) {
+      if (__builtin_expect(dma_buf && k0 + C::BN <= M, 1)) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+#pragma unroll
+          for (int i = 0; i < C::DMA_PER_TILE; ++i) {
+            if (C::DMA_INSTS % kWaves != 0 && i * kWaves + w >= C::DMA_INSTS) break;
+            dma16_buf(dma_rsrc[which], dma_off[which],
+                      (uint32_t)(k0 + i * kWaves * C::RPI) * C::ROWB,
+                      (which ? vdst : kdst) + (i * kWaves + w) * 1024);
+          }
+        }
+        return;
+      }
+    }
+    dma_half(t, kdst, 0);
+    dma_half(t, vdst, 1);
   };
   auto load_stage = [&](int t) {          // staged: global -> registers
     const int k0 = t * C::BN;
@@ -400,7 +445,12 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // MFMAs follow it, so the exp work of the second half can overlap the
   // matrix-core work of the first.
   auto tile_softmax_pv = [&](Scores& sc, lds_char* vbuf_lds) {
-    float mloc[C::QB];
+    // The reference moves only when some row's maximum passes it by more
+    // than kLazy (log2 units).  The test is monotone in the score, so asking
+    // it of each lane's own maximum gives the same wave-wide answer as asking
+    // it of the row maxima; the cross-lane reduction is only needed when the
+    // reference moves.
+    float mlane[C::QB];
     bool bump = false;
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
@@ -409,24 +459,21 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      mx = rows_max(mx);
-      mloc[qb] = mx;
+      mlane[qb] = mx;
       bump = bump || ((mx - m_run[qb]) * sl > kLazy);
     }
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {   // wave-uniform, rare
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mloc[qb]);
+        const float m_new = fmaxf(m_run[qb], rows_max(mlane[qb]));
         const float alpha = (m_new == kNegInf) ? 1.f : exp2_hw((m_run[qb] - m_new) * sl);
         m_run[qb] = m_new;
+        nmsl[qb] = (m_new == kNegInf) ? 0.f : -(m_new * sl);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int i = 0; i < C::NDB; ++i) acc[qb][i] *= alpha;
       }
     }
-    float msl[C::QB];
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) msl[qb] = (m_run[qb] == kNegInf) ? 0.f : m_run[qb] * sl;
     if constexpr (H16) {
 #pragma unroll
       for (int c = 0; c < C::NKB / 2; ++c) {
@@ -436,7 +483,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
           float pp[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pp[e] = exp2_hw(fmaf(sc[qb][2 * c + (e >> 2)][e & 3], sl, -msl[qb]));
+            pp[e] = exp2_hw(fmaf(sc[qb][2 * c + (e >> 2)][e & 3], sl, nmsl[qb]));
             l_run[qb] += pp[e];
           }
           bop[qb] = pack16x8<ET>(pp);
@@ -478,7 +525,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
         for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pf[qb][r] = exp2_hw(fmaf(sc[qb][kb][r], sl, -msl[qb]));
+            pf[qb][r] = exp2_hw(fmaf(sc[qb][kb][r], sl, nmsl[qb]));
             l_run[qb] += pf[qb][r];
           }
 #pragma unroll
@@ -506,8 +553,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   auto step = [&](int t, int tn, lds_char* krd, lds_char* vrd, lds_char* kwr, lds_char* vwr) {
     if (tn < ntiles) {
       if constexpr (DIRECT) {
-        dma_half(tn, kwr, 0);
-        dma_half(tn, vwr, 1);
+        dma_tile(tn, kwr, vwr);
       } else {
         load_stage(tn);
       }
@@ -526,8 +572,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   int t = next_tile(t_first);
   if (t < ntiles) {
     if constexpr (DIRECT) {
-      dma_half(t, k0s, 0);
-      dma_half(t, v0s, 1);
+      dma_tile(t, k0s, v0s);
     } else {
       load_stage(t);
       store_stage(k0s, v0s);
