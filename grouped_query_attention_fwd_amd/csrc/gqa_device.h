@@ -157,15 +157,6 @@ __device__ __forceinline__ void dma16(const void* gsrc, lds_char* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// The same copy through a buffer descriptor: the source of a lane is the
-// descriptor's base + `soff` (wave-uniform, a scalar register) + `voff`
-// (per lane).  Callers keep every source inside the descriptor's range.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                          lds_char* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, soff, 0, 0);
-}
-
 // LDS accessors on a byte offset into a shared buffer.
 __device__ __forceinline__ void lds_st16(lds_char* base, uint32_t off, u32x4 v) {
   *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(base + off) = v;

@@ -19,10 +19,13 @@
 //   * K and V tiles of BN keys are double-buffered in LDS, as four distinct
 //     LDS objects with the tile loop unrolled by two (every access names its
 //     stage).  16-bit tiles whose rows need no column padding go straight
-//     from global memory to LDS with global_load_lds_dwordx4 (no staging
-//     registers); the XOR swizzle of the LDS rows is applied by permuting
-//     each lane's global source.  Other cases stage through registers.  The
-//     next tile's copy is issued before the current tile's math.
+//     from global memory to LDS (no staging registers): whole tiles with
+//     buffer_load_dwordx4 ... lds from a descriptor, a scalar row offset and
+//     a loop-invariant lane offset (no vector instructions), a ragged last
+//     tile with global_load_lds_dwordx4 on clamped rows.  The XOR swizzle of
+//     the LDS rows is applied by permuting each lane's global source.  Other
+//     cases stage through registers.  The next tile's copy is issued before
+//     the current tile's math.
 //   * Each wave owns 16*QB query rows.  S^T = K Q^T and O^T = V^T P^T run on
 //     v_mfma_f32_16x16x32_bf16 / _f16 (16-bit inputs) or
 //     v_mfma_f32_16x16x4f32 (fp32 inputs); V^T is read with the transposing
@@ -106,6 +109,17 @@ struct PreCfg {
   static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
   static_assert(!H16 || (BN % RPI == 0), "direct copy must cover whole rows");
 };
+
+// Direct global -> LDS copy of 16 bytes per lane through a buffer
+// descriptor (buffer_load_dwordx4 ... lds): the source of a lane is the
+// descriptor's base + `soff` (wave-uniform, a scalar register) + `voff`
+// (per lane); the LDS destination is `lds_base` + 16 * lane.  Callers keep
+// every source inside the descriptor's range.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          lds_char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, soff, 0, 0);
+}
 
 template <bool H16, int DP>
 __device__ __forceinline__ uint32_t k_off(int row, int chunk) {
