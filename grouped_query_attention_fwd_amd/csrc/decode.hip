@@ -424,8 +424,13 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     u32x4 v[C::VLOADS];       // V rows, coalesced 16-byte pieces
   };
   // Issue every load of the chunk at `base` (K first, then V).  Addresses
-  // are clamped to valid rows; rows past the split are zeroed (V) or masked
-  // to -inf later (K).
+  // are clamped to valid rows.  Nothing here touches the loaded values, so
+  // the next chunk's loads stay in flight while the current chunk is
+  // computed: rows past the split are zeroed when V is written to LDS or
+  // masked to -inf (K), and padded d is zeroed when K feeds the MFMA.
+  bool kdv[C::QCH];
+#pragma unroll
+  for (int u = 0; u < C::QCH; ++u) kdv[u] = EXACT || (H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg)) < D;
   auto load_chunk = [&](int base) {
     Chunk ch;
     // group kb of the chunk starts at key base + 16 kb; a group wholly past
@@ -450,7 +455,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
           ch.k[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
         } else {
           const bool dv = d0 < D;
-          ch.k[kb][u] = sel16(dv, ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT));
+          ch.k[kb][u] = ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT);  // zeroed at use
         }
       }
     }
@@ -466,8 +471,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       const int d0 = chunk * (16 / C::ELT);
       const bool ok = key < k_end && (EXACT || d0 < D);
       const size_t roff = goff[grp] + (size_t)(min(key, klast) - g16[grp]) * D * C::ELT;
-      const u32x4 x = ld16(vp + roff + (size_t)(ok ? d0 : 0) * C::ELT);
-      ch.v[it] = sel16(ok, x);
+      ch.v[it] = ld16(vp + roff + (size_t)(ok ? d0 : 0) * C::ELT);  // zeroed at use
     }
     return ch;
   };
@@ -488,17 +492,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     if (r >= nround) r -= nround;
     return k_begin + r * kstride + w * C::KC;
   };
-  int t_round = 0;
-  int base = base_of(0);
-  Chunk cur;
-  if (nround > 0) cur = load_chunk(base);
-  while (t_round < nround) {
-    const bool more = t_round + 1 < nround;
-    const int nb = more ? base_of(t_round + 1) : base;
-    Chunk nxt;
-    if constexpr (C::PREFETCH) {
-      if (more) nxt = load_chunk(nb);
-    }
+  // One chunk of keys: S, softmax, O += V^T P^T (the chunk's loads were
+  // issued earlier).
+  auto compute = [&](const Chunk& cur, const int base) {
     const auto& kop = cur.k;
     const auto& vreg = cur.v;
     // ---- S^T = K Q^T ------------------------------------------------------
@@ -509,11 +505,12 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
         if constexpr (H16) {
-          c = mma16<ET>(kop[kb][u], qop[u], c);
+          c = mma16<ET>(EXACT ? kop[kb][u] : sel16(kdv[u], kop[kb][u]), qop[u], c);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            c = mfma_f32(__uint_as_float(kop[kb][u][e]), __uint_as_float(qop[u][e]), c);
+            c = mfma_f32(EXACT || kdv[u] ? __uint_as_float(kop[kb][u][e]) : 0.f,
+                         __uint_as_float(qop[u][e]), c);
         }
       }
       sc[kb] = c;
@@ -524,7 +521,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       const int piece = it * 64 + lane;
       const int row = piece / C::CPR;
       const int chunk = piece - row * C::CPR;
-      lds_st16(vl, v_off<H16, DP>(row, chunk), vreg[it]);
+      const bool ok = base + row < k_end && (EXACT || chunk * (16 / C::ELT) < D);
+      lds_st16(vl, v_off<H16, DP>(row, chunk), sel16(ok, vreg[it]));
     }
     // ---- visibility + online softmax --------------------------------------
     float mloc = kNegInf;
@@ -599,14 +597,34 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (!more) break;
-    if constexpr (C::PREFETCH) {
-      cur = nxt;
-    } else {
-      cur = load_chunk(nb);
+  };
+  if constexpr (C::PREFETCH) {
+    // Two chunk buffers used in turn: the next chunk's loads are in flight
+    // while this one is computed.  No chunk is ever copied from one buffer
+    // to the other, and inside the loop every load is unconditional, so the
+    // compiler's load counters stay exact: a copy, or a load issued on one
+    // path only, would make it wait for the chunk in flight as well.
+    Chunk ca, cb;
+    int t = 0;
+    if (nround > 0) ca = load_chunk(base_of(0));
+    for (; t + 2 < nround; t += 2) {
+      cb = load_chunk(base_of(t + 1));
+      compute(ca, base_of(t));
+      ca = load_chunk(base_of(t + 2));
+      compute(cb, base_of(t + 1));
     }
-    base = nb;
-    ++t_round;
+    if (t + 1 < nround) {
+      cb = load_chunk(base_of(t + 1));
+      compute(ca, base_of(t));
+      compute(cb, base_of(t + 1));
+    } else if (t < nround) {
+      compute(ca, base_of(t));
+    }
+  } else {
+    for (int t = 0; t < nround; ++t) {
+      const int b0 = base_of(t);
+      compute(load_chunk(b0), b0);
+    }
   }
 
   // ---- merge the waves through LDS -----------------------------------
