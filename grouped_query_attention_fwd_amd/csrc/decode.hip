@@ -371,7 +371,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   int k_end = __builtin_amdgcn_readfirstlane(pc.k_end);
   if constexpr (PAGED) k_end = min(k_end, max(0, a.kv_len[b]));   // this sequence's keys
 
-  // K/V rows are addressed per aligned group of 16 keys.  `group_off(g16)`
+  // K/V rows are addressed per aligned group of 16 keys.  `group_off(g16, e)`
   // is the byte offset of the row of key g16 (a multiple of 16) inside the
   // K or V buffer; the other 15 keys of the group follow it contiguously.
   // The group start is wave-uniform, so a paged lookup is one scalar load.
@@ -379,12 +379,14 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   const char* kp = reinterpret_cast<const char*>(a.k) + kv_base * C::ELT;
   const char* vp = reinterpret_cast<const char*>(a.v) + kv_base * C::ELT;
   const int32_t* __restrict__ btab = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
-  auto group_off = [&](int g16) -> size_t {
+  // `entry` is the block-table entry of the group (paged only), read ahead
+  // of time by tab_of below.
+  auto group_off = [&](int g16, int entry) -> size_t {
     if constexpr (PAGED) {
       const int blk = g16 / a.block_size;
       // a block id outside the pool is clamped into it: memory stays safe,
       // the values are then the caller's responsibility
-      const int phys = min(max(btab[blk], 0), a.num_blocks - 1);
+      const int phys = min(max(entry, 0), a.num_blocks - 1);
       return (((size_t)phys * a.H_kv + j) * a.block_size + (g16 - blk * a.block_size)) *
              (size_t)D * C::ELT;
     } else {
@@ -431,18 +433,36 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   bool kdv[C::QCH];
 #pragma unroll
   for (int u = 0; u < C::QCH; ++u) kdv[u] = EXACT || (H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg)) < D;
-  auto load_chunk = [&](int base) {
+  // Group kb of the chunk at `base` starts at key base + 16 kb; a group
+  // wholly past the split is redirected to the split's last group (its rows
+  // are masked out later, only the addresses must stay valid).
+  const int glast = klast & ~15;
+  // The block-table entries of a chunk's groups (paged): scalar loads issued
+  // one chunk ahead of the chunk's own loads, so that no load of K or V
+  // waits for a table read.
+  struct Tab {
+    int e[C::NKB];
+  };
+  auto tab_of = [&](int base) {
+    Tab tb;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      if constexpr (PAGED) {
+        tb.e[kb] = btab[min(base + 16 * kb, glast) / a.block_size];
+      } else {
+        tb.e[kb] = 0;
+      }
+    }
+    return tb;
+  };
+  auto load_chunk = [&](int base, const Tab& tb) {
     Chunk ch;
-    // group kb of the chunk starts at key base + 16 kb; a group wholly past
-    // the split is redirected to the split's last group (its rows are
-    // masked out later, only the addresses must stay valid)
-    const int glast = klast & ~15;
     int g16[C::NKB];
     size_t goff[C::NKB];
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       g16[kb] = min(base + 16 * kb, glast);
-      goff[kb] = group_off(g16[kb]);
+      goff[kb] = group_off(g16[kb], tb.e[kb]);
     }
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
@@ -604,17 +624,30 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     // to the other, and inside the loop every load is unconditional, so the
     // compiler's load counters stay exact: a copy, or a load issued on one
     // path only, would make it wait for the chunk in flight as well.
+    // The scheduling barriers keep the compiler from sinking a chunk's
+    // loads below the previous chunk's math (it does, to save registers).
     Chunk ca, cb;
+    Tab ta, tb;  // tables of the next chunk to load into ca / cb
+    auto tab_at = [&](int t) { return tab_of(base_of(min(t, nround - 1))); };
     int t = 0;
-    if (nround > 0) ca = load_chunk(base_of(0));
+    if (nround > 0) {
+      ta = tab_at(0);
+      ca = load_chunk(base_of(0), ta);
+      tb = tab_at(1);
+    }
     for (; t + 2 < nround; t += 2) {
-      cb = load_chunk(base_of(t + 1));
+      cb = load_chunk(base_of(t + 1), tb);
+      ta = tab_at(t + 2);
+      __builtin_amdgcn_sched_barrier(0);
       compute(ca, base_of(t));
-      ca = load_chunk(base_of(t + 2));
+      ca = load_chunk(base_of(t + 2), ta);
+      tb = tab_at(t + 3);
+      __builtin_amdgcn_sched_barrier(0);
       compute(cb, base_of(t + 1));
     }
     if (t + 1 < nround) {
-      cb = load_chunk(base_of(t + 1));
+      cb = load_chunk(base_of(t + 1), tb);
+      __builtin_amdgcn_sched_barrier(0);
       compute(ca, base_of(t));
       compute(cb, base_of(t + 1));
     } else if (t < nround) {
@@ -623,7 +656,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   } else {
     for (int t = 0; t < nround; ++t) {
       const int b0 = base_of(t);
-      compute(load_chunk(b0), b0);
+      compute(load_chunk(b0, tab_of(b0)), b0);
     }
   }
 
