@@ -458,6 +458,16 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // The weights are formed one 32-key half at a time and each half's P.V
   // MFMAs follow it, so the exp work of the second half can overlap the
   // matrix-core work of the first.
+  // Byte offsets of this lane's transposing V reads: row 4 qg + c16 / 4 of
+  // the tile (plus a multiple of 16 rows, which keeps the swizzle), 16-byte
+  // chunk 2 db + (c16 % 4) / 2, half (c16 % 2).  Loop-invariant.
+  uint32_t vt_off[C::NDB];
+  if constexpr (H16) {
+    const int vr = 4 * qg + (c16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+      vt_off[db] = v_off<H16, DP>(vr, 2 * db + ((c16 & 3) >> 1)) + ((c16 & 1) << 3);
+  }
   auto tile_softmax_pv = [&](Scores& sc, lds_char* vbuf_lds) {
     // The reference moves only when some row's maximum passes it by more
     // than kLazy (log2 units).  The test is monotone in the score, so asking
@@ -502,14 +512,10 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
           }
           bop[qb] = pack16x8<ET>(pp);
         }
-        const int row_a = 32 * c + 4 * qg + (c16 >> 2);
-        const int row_b = row_a + 16;
-        const int within = (c16 & 1) << 3;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const int chunk = 2 * db + ((c16 & 3) >> 1);
-          const i16x4 ta = lds_ld_tr16(vbuf_lds, v_off<H16, DP>(row_a, chunk) + within);
-          const i16x4 tb = lds_ld_tr16(vbuf_lds, v_off<H16, DP>(row_b, chunk) + within);
+          const i16x4 ta = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c) * C::ROWB);
+          const i16x4 tb = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c + 16) * C::ROWB);
           const u32x4 vop = concat16(ta, tb);
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mma16<ET>(vop, bop[qb], acc[qb][db]);
