@@ -20,7 +20,9 @@
 // each sequence's own length ends its key range).  Per chunk a wave
 //   1. loads K rows straight into MFMA operand registers (16 bytes per lane)
 //      and V rows with coalesced 16-byte loads, all issued up front with
-//      clamped (always valid) addresses so nothing waits on a branch;
+//      clamped (always valid) addresses so nothing waits on a branch, one
+//      chunk ahead of the math (two register buffers used in turn; a paged
+//      cache's block-table entries are read one chunk further ahead);
 //   2. forms S^T = K Q^T on the matrix cores (keys x heads);
 //   3. copies the V chunk into its private, XOR-swizzled LDS area;
 //   4. runs the online softmax with scores scaled by log2(e)/sqrt(D) and the
