@@ -297,8 +297,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // offset (scalar register) and a per-lane offset that does not change from
   // tile to tile (the swizzle depends only on the row's low bits, which the
   // advance of kWaves * RPI rows per instruction leaves alone for D <= 128),
-  // so such a copy costs no vector instructions.  Slabs of 2 GB or more take
-  // the clamped path below.
+  // so such a copy costs no vector instructions.  Slabs of 2^31 bytes or
+  // more take the clamped path below.
   constexpr bool kDmaInvariant = DIRECT && ((kWaves * C::RPI) % (C::KSWZ + 1) == 0) &&
                                  ((kWaves * C::RPI) % (C::VSWZ + 1) == 0);
   const bool dma_buf = kDmaInvariant && (long long)M * C::ROWB <= 0x7fffffffLL;
@@ -449,15 +449,6 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       }
     }
   };
-  // Online softmax and O^T += V^T P^T for one tile.
-  // Weights are p = 2^(s*sl - m_ref*sl) against a per-row reference max
-  // m_ref (m_run).  The reference, and with it acc and l, only moves when
-  // some row of the wave has a score more than kLazy (log2 units) above it,
-  // so p <= 2^kLazy and most tiles skip the rescale; softmax does not depend
-  // on the reference, so the result is the same.
-  // The weights are formed one 32-key half at a time and each half's P.V
-  // MFMAs follow it, so the exp work of the second half can overlap the
-  // matrix-core work of the first.
   // Byte offsets of this lane's transposing V reads: row 4 qg + c16 / 4 of
   // the tile (plus a multiple of 16 rows, which keeps the swizzle), 16-byte
   // chunk 2 db + (c16 % 4) / 2, half (c16 % 2).  Loop-invariant.
@@ -468,6 +459,15 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     for (int db = 0; db < C::NDB; ++db)
       vt_off[db] = v_off<H16, DP>(vr, 2 * db + ((c16 & 3) >> 1)) + ((c16 & 1) << 3);
   }
+  // Online softmax and O^T += V^T P^T for one tile.
+  // Weights are p = 2^(s*sl - m_ref*sl) against a per-row reference max
+  // m_ref (m_run).  The reference, and with it acc and l, only moves when
+  // some row of the wave has a score more than kLazy (log2 units) above it,
+  // so p <= 2^kLazy and most tiles skip the rescale; softmax does not depend
+  // on the reference, so the result is the same.
+  // The weights are formed one 32-key half at a time and each half's P.V
+  // MFMAs follow it, so the exp work of the second half can overlap the
+  // matrix-core work of the first.
   auto tile_softmax_pv = [&](Scores& sc, lds_char* vbuf_lds) {
     // The reference moves only when some row's maximum passes it by more
     // than kLazy (log2 units).  The test is monotone in the score, so asking
