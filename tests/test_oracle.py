@@ -456,6 +456,35 @@ def pin_band_wide_window_is_causal(orc):
                                orc.gqa(q, k, v, causal=True), rtol=0, atol=0)
 
 
+def pin_band_window_width(orc):
+    """The width of the band, counted without restating its inequalities.
+    With K = 0 every visible key gets the same weight (pin_zero_keys_give_mean),
+    so a V that holds the key index j in channel 0 and j^2 in channel 1 makes
+    the output the mean and the mean square of the visible key indices.  The
+    W consecutive integers a .. a+W-1 have mean a + (W-1)/2 and variance
+    (W^2 - 1)/12, so an interior row with window_left = W - 1 and right edge
+    0 (W keys ending at its position p = i + q_offset) must give mean
+    p - (W-1)/2 and variance (W^2-1)/12, and a two-sided band (wl, wr) must
+    give W = wl + wr + 1 keys centred at p + (wr - wl)/2."""
+    N, M, D = 12, 40, 2
+    j = np.arange(M, dtype=np.float64)
+    v = np.stack([j, j * j], axis=-1)[None, None]              # [1, 1, M, 2]
+    k = np.zeros((1, 1, M, D))
+    q = rng(75).standard_normal((1, 2, N, D))
+    for q_off, wl, wr in [(20, 0, 0), (20, 1, 0), (20, 4, 0), (20, 7, 0), (15, 2, 3),
+                          (10, 0, 5), (25, 6, 6)]:
+        out = orc.gqa_band(q, k, v, None, q_off, wl, wr)
+        W = wl + wr + 1
+        for i in range(N):
+            p = i + q_off
+            if p - wl < 0 or p + wr >= M:
+                continue                       # not an interior row
+            mean = out[0, 0, i, 0]
+            var = out[0, 0, i, 1] - mean * mean
+            assert abs(mean - (p + (wr - wl) / 2)) < 1e-9, (q_off, wl, wr, i, mean)
+            assert abs(var - (W * W - 1) / 12) < 1e-7, (q_off, wl, wr, i, var)
+
+
 PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
         pin_mha_equals_per_head, pin_mqa_brute_force, pin_single_key,
         pin_two_keys_closed_form, pin_scale_exact, pin_zero_keys_give_mean,
@@ -464,7 +493,8 @@ PINS = [pin_worked_example_shape, pin_library_crosscheck, pin_brute_force,
         pin_key_permutation, pin_empty_row_is_nan, pin_rejects_bad_group,
         pin_paged_brute_force, pin_paged_identity_table, pin_paged_length_is_truncation,
         pin_paged_block_permutation, pin_band_causal_is_causal,
-        pin_band_bottom_right_is_a_chunk, pin_band_brute_force, pin_band_wide_window_is_causal]
+        pin_band_bottom_right_is_a_chunk, pin_band_brute_force, pin_band_wide_window_is_causal,
+        pin_band_window_width]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)

@@ -29,7 +29,8 @@ import torch
 
 __all__ = ["Workload", "WORKLOADS", "GROUP_SWEEP", "by_name", "make_inputs", "random_case",
            "PagedWorkload", "PAGED_WORKLOADS", "paged_by_name", "make_paged_inputs",
-           "random_paged_case"]
+           "random_paged_case", "KEY_PATTERN_MOD", "KEY_PATTERN_POISON", "key_pattern_rows",
+           "key_coverage_inputs", "key_coverage_paged"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -254,3 +255,55 @@ def random_paged_case(seed, B, H, H_kv, D, block_size, max_len, dtype=torch.floa
 def make_paged_inputs(w: PagedWorkload):
     return random_paged_case(w.seed, w.B, w.H, w.H_kv, w.D, w.block_size, w.max_len,
                              w.torch_dtype, lengths=w.lengths, slack_blocks=0)
+
+
+# ------------------------------------------------- key-coverage check inputs
+# V holds small integers that vary with the key index without a short
+# period, and K is zero, so every visible key gets the same weight and the
+# attention output is the plain mean of V over the visible keys: a closed
+# form that sees a skipped, repeated or shifted key.  All values are exact
+# in bf16, fp16 and fp32, and sums over up to 67,000 keys stay below 2^24,
+# so every partial sum in fp32 is exact too.
+KEY_PATTERN_MOD = 251        # a prime, so no power-of-two key range is a whole period
+KEY_PATTERN_POISON = 255     # for pool rows that no sequence owns (exact in 16 bits)
+
+
+def key_pattern_rows(b, H_kv, m0, m1, D):
+    """int32 [H_kv, m1 - m0, D]: V[b, j, m, d] = (7 m + 13 d + 29 j + 31 b) mod 251
+    for keys m0 <= m < m1."""
+    j = torch.arange(H_kv, dtype=torch.int64)[:, None, None]
+    m = torch.arange(m0, m1, dtype=torch.int64)[None, :, None]
+    d = torch.arange(D, dtype=torch.int64)[None, None, :]
+    return ((7 * m + 13 * d + 29 * j + 31 * b) % KEY_PATTERN_MOD).to(torch.int32)
+
+
+def key_coverage_inputs(B, H, H_kv, N, M, D, dtype):
+    """(q, k, v) CPU tensors for a key-coverage check: q i.i.d. N(0,1) (its
+    values do not matter, K is zero), k = 0, v = key_pattern_rows."""
+    gen = torch.Generator().manual_seed(7919)
+    q = torch.randn((B, H, N, D), generator=gen, dtype=torch.float32).to(dtype)
+    k = torch.zeros((B, H_kv, M, D), dtype=dtype)
+    v = torch.empty((B, H_kv, M, D), dtype=dtype)
+    for b in range(B):
+        v[b] = key_pattern_rows(b, H_kv, 0, M, D).to(dtype)
+    return q, k, v
+
+
+def key_coverage_paged(w: PagedWorkload):
+    """(q, k_pool, v_pool, block_table, kv_len) for a key-coverage check of a
+    paged workload: its block table and lengths, K zero, and the pool V
+    filled so that key t of sequence b holds key_pattern_rows(b, ...)[:, t];
+    pool rows owned by no sequence hold KEY_PATTERN_POISON."""
+    q, kp, vp, table, lens = make_paged_inputs(w)
+    dtype = w.torch_dtype
+    kp = torch.zeros_like(kp)
+    vp = torch.full(vp.shape, KEY_PATTERN_POISON, dtype=dtype)
+    bs = w.block_size
+    for b in range(w.B):
+        n = int(lens[b])
+        rows = key_pattern_rows(b, w.H_kv, 0, n, w.D).to(dtype)      # [H_kv, n, D]
+        for t0 in range(0, n, bs):
+            blk = int(table[b, t0 // bs])
+            t1 = min(n, t0 + bs)
+            vp[blk, :, : t1 - t0, :] = rows[:, t0:t1, :]
+    return q, kp, vp, table, lens
