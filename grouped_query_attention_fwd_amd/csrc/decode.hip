@@ -345,7 +345,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   if (PAGED && a.pieces > 0) {
     if (!paged_piece(a, blockIdx.x, pc)) return;  // uniform: no piece for this workgroup
   } else {
-    pc.unit = blockIdx.x;
+    pc.unit = (int)(blockIdx.x + gridDim.x * blockIdx.z);
+    if (pc.unit >= a.B * a.H_kv * a.head_chunks) return;  // past a folded grid's end (uniform)
     if (a.xcd_group) {
       const int x = pc.unit & 7, i = pc.unit >> 3;
       pc.unit = ((i / a.head_chunks) * 8 + x) * a.head_chunks + i % a.head_chunks;
@@ -742,7 +743,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
 template <int ET, int DP, bool EXACT, bool OUTF32>
 hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * a.head_chunks;
-  const dim3 grid = a.pieces > 0 ? dim3(a.pieces) : dim3(units, a.splits);
+  const dim3 grid = a.pieces > 0 ? dim3(a.pieces) : fold_grid(units, (unsigned)a.splits);
   if (a.block_table) {  // the paged form takes no mask
     hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
   } else if (a.mask) {

@@ -68,6 +68,18 @@ struct PrefillArgs {
   bool out_f32;
 };
 
+// Largest grid x dimension a launch uses (a multiple of the 8 XCDs, so the
+// XCD of workgroup L = x + kMaxGridX * z stays L % 8).  Launches with more
+// workgroups fold the rest into grid z; the kernels rebuild L from both and
+// drop the workgroups past the end.  This keeps every grid dimension far
+// below the runtime's limit of 2^32 work-items.
+constexpr unsigned kMaxGridX = 1u << 16;
+inline dim3 fold_grid(long n, unsigned y) {
+  const unsigned x = n > (long)kMaxGridX ? kMaxGridX : (unsigned)n;
+  const unsigned z = (unsigned)((n + x - 1) / x);
+  return dim3(x, y, z);
+}
+
 // Decode workspace layout: kCounterBytes of arrival counters (one per unit,
 // zero between calls), then the split partials.  The counter area has the
 // same place and size for every plan, so partials never land on it.

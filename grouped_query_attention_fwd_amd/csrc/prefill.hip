@@ -172,7 +172,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
   // Order 2 is for blocks of very unequal weight (causal with N close to
   // M): each XCD runs its units side by side, heaviest blocks of all of them
   // first, so the light blocks fill the end (longest-processing-time first).
-  const int L = blockIdx.x;
+  const int L = (int)(blockIdx.x + gridDim.x * blockIdx.z);
+  if (L >= units * npb) return;  // the end of a folded grid (workgroup-uniform)
   int unit, pbi;
   if (order) {
     const int x = L & 7;
@@ -657,9 +658,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
 constexpr int kMergeThreads = 128;
 template <int ET, bool OUTF32>
 __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArgs a) {
-  const size_t row = blockIdx.x;
+  const size_t row = (size_t)blockIdx.x + (size_t)gridDim.x * blockIdx.z;
   const int d = blockIdx.y * kMergeThreads + threadIdx.x;
-  if (d >= a.D) return;
+  if (d >= a.D || row >= (size_t)a.B * a.H * a.N) return;
   const float sl = kLog2e / sqrtf((float)a.D);
   const size_t stride = (size_t)a.D + 4;
   const int S = a.splits;
@@ -717,13 +718,13 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
     if (2 * max(first, 1LL) <= min(last, (long long)a.M)) order = 2;
   }
   hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32>),
-                     dim3((unsigned)blocks, (unsigned)a.splits), dim3(kThreads), 0, stream, a, HG,
+                     fold_grid(blocks, (unsigned)a.splits), dim3(kThreads), 0, stream, a, HG,
                      units, npb, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const long rows = (long)a.B * a.H * a.N;
   hipLaunchKernelGGL((prefill_merge_kernel<ET, OUTF32>),
-                     dim3((unsigned)rows, (unsigned)((a.D + kMergeThreads - 1) / kMergeThreads)),
+                     fold_grid(rows, (unsigned)((a.D + kMergeThreads - 1) / kMergeThreads)),
                      dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }

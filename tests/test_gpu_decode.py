@@ -250,3 +250,9 @@ def test_decode_mistral7b_fp16_full():
     out = gqa.decode(*to_dev(q, k, v))
     mx, rr = compare(out, oracle_out(q, k, v), TOL[torch.float16], w.name)
     say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")
+
+
+def test_decode_grid_of_more_than_65536_workgroups():
+    """8200 batch rows of 8 KV heads (g = 1): 65,600 units, one workgroup
+    each, more than one grid row holds, so the launch folds them into grid z."""
+    run_case(91, 8200, 8, 8, 3, 8, torch.bfloat16)

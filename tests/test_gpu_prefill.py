@@ -154,3 +154,14 @@ def test_prefill_causal_n4096_full_sampled(name):
         ref = oracle.gqa(np64(qs[b:b + 1]), np64(k[b:b + 1]), np64(v[b:b + 1]), np64(m[b:b + 1]))
         mx, rr = compare(out[b:b + 1, :, rows, :], ref, TOL[w.torch_dtype], f"{w.name} b={b}")
         say(f"  b={b} max abs err {mx:.3e} rel rms {rr:.3e}")
+
+
+def test_prefill_grid_of_more_than_65536_workgroups():
+    """1040 query heads (g = 1) of 4100 fp32 positions: 65 blocks of 64
+    positions per head, 67,600 workgroups, more than one grid row holds, so
+    the launch folds them into grid z."""
+    B, H, H_kv, N, M, D = 1, 1040, 1040, 4100, 5, 4
+    say("prefill folded grid")
+    q, k, v, _ = workloads.random_case(90, B, H, H_kv, N, M, D, torch.float32)
+    out = gqa.prefill(*to_dev(q, k, v), causal=True)
+    compare(out, oracle_out(q, k, v, causal=True), TOL[torch.float32], "folded grid")
