@@ -18,6 +18,10 @@ are not on a GPU the call raises.
                  workspace=None)
         q [B,H,1,D], pools [num_blocks,H_kv,block_size,D], block_table
         [B,max_blocks] int32, kv_len [B] int32
+    decode_noalloc(q, k, v, mask=None, out=None, out_dtype=None)
+        decode with no workspace and no allocation inside the library (a fixed
+        per-GPU scratch area of DECODE_NOALLOC_SCRATCH_BYTES; calls that may
+        overlap on one GPU race on it)
     decode_workspace_size(B, H, H_kv, M, D) -> bytes
     decode_paged_workspace_size(B, H, H_kv, max_blocks, block_size, D) -> bytes
     status_string(code) -> str
@@ -32,21 +36,24 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["decode", "decode_paged", "prefill", "prefill_band", "decode_op", "decode_paged_op",
+__all__ = ["decode", "decode_noalloc", "decode_paged", "prefill", "prefill_band", "decode_op", "decode_paged_op",
            "prefill_op", "prefill_band_op",
            "decode_workspace_size", "decode_paged_workspace_size", "status_string",
-           "library_path", "GQAError", "load_library", "DECODE_COUNTER_BYTES"]
+           "library_path", "GQAError", "load_library", "DECODE_COUNTER_BYTES",
+           "DECODE_NOALLOC_SCRATCH_BYTES"]
 
 # Bytes of arrival counters at the start of a decode workspace; they must be
 # zero before the first call, and every call leaves them zero.
 DECODE_COUNTER_BYTES = 16384
+# Size of the fixed per-GPU scratch area of decode_noalloc.
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgqa.so")
 _lib = None
 
 GQA_F32, GQA_BF16, GQA_F16 = 0, 1, 2
-_STATUS_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9}
+_STATUS_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 9, 10}
 
 
 class GQAError(RuntimeError):
@@ -72,6 +79,8 @@ def load_library():
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.gqa_decode.restype = i
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.gqa_decode_noalloc.restype = i
     lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, vp]
     lib.gqa_prefill.restype = i
     lib.gqa_prefill_band.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i, vp]
@@ -337,6 +346,30 @@ def decode(q, k, v, mask=None, out=None, out_dtype=None, workspace=None):
     lib, args, out, _ws = _prepare_decode(q, k, v, mask, out, out_dtype, workspace, shared=True)
     with torch.cuda.device(q.device):
         _check(lib.gqa_decode(*args, torch.cuda.current_stream(q.device).cuda_stream))
+    return out
+
+
+def decode_noalloc(q, k, v, mask=None, out=None, out_dtype=None):
+    """decode() through gqa_decode_noalloc: no workspace, and the library
+    allocates nothing (its key-split scratch is a fixed area of
+    DECODE_NOALLOC_SCRATCH_BYTES per GPU; larger problems raise ValueError).
+    Calls that may overlap on one GPU race on that area.  `out` may be given
+    to avoid the one allocation this binding would otherwise make."""
+    torch = _torch()
+    _check_tensors(q, k, v, mask)
+    B, H, N, D = q.shape
+    _, H_kv, M, _ = k.shape
+    if N != 1:
+        raise ValueError("decode takes one query position (q [B,H,1,D])")
+    if mask is not None and tuple(mask.shape) != (B, 1, M):
+        raise ValueError("decode mask must be [B,1,M]")
+    out = _out(q, out, out_dtype, (B, H, 1, D))
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.gqa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), _mask_ptr(mask),
+                                      out.data_ptr(), B, H, H_kv, M, D, _dtype_code(q.dtype),
+                                      _dtype_code(out.dtype),
+                                      torch.cuda.current_stream(q.device).cuda_stream))
     return out
 
 

@@ -9,6 +9,12 @@ static_assert(gqa::kCounterBytes == GQA_DECODE_COUNTER_BYTES, "counter area size
 #include <limits.h>
 
 #include <initializer_list>
+#include <mutex>
+
+// The fixed scratch area of gqa_decode_noalloc: arrival counters, then the
+// key-split partials, as in a gqa_decode workspace.
+constexpr size_t kScratchBytes = GQA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -56,53 +62,26 @@ gqa_status_t check_common(const void* q, const void* k, const void* v, const voi
   return GQA_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-const char* gqa_status_string(gqa_status_t s) {
-  switch (s) {
-    case GQA_OK: return "success";
-    case GQA_ERR_NULL: return "a required pointer is NULL";
-    case GQA_ERR_SHAPE: return "invalid shape (a dimension < 1, or sizes exceed the limits)";
-    case GQA_ERR_GROUP: return "H is not a multiple of H_kv";
-    case GQA_ERR_DTYPE: return "unsupported dtype combination";
-    case GQA_ERR_ALIGN: return "q/k/v/out/workspace must be 16-byte aligned";
-    case GQA_ERR_UNSUPPORTED:
-      return "unsupported size (need D <= 256, D*sizeof(dtype) % 16 == 0 and, paged, block_size % 16 == 0)";
-    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
-    case GQA_ERR_HIP: return "HIP runtime error";
-    case GQA_ERR_ALIAS: return "out overlaps an input or the workspace";
-  }
-  return "unknown status";
-}
-
-size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D) {
-  if (B < 1 || H < 1 || H_kv < 1 || M < 1 || D < 1 || H % H_kv != 0) return 0;
-  const long long kvrows = mul_checked({B, H_kv, M});
-  if (kvrows < 0 || kvrows >= INT_MAX || mul_checked({B, H}) >= INT_MAX) return 0;
-  return gqa::plan_decode(B, H, H_kv, M, D, false).workspace_bytes;
-}
-
-gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8_t* mask,
-                        void* out, int B, int H, int H_kv, int M, int D, gqa_dtype_t in_dtype,
-                        gqa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
-  if (st != GQA_OK) return st;
-  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D, false);
-  if (plan.workspace_bytes > 0) {
-    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return GQA_ERR_ALIGN;
-  }
+// out must not overlap q, k, v or the mask of a decode call.
+gqa_status_t check_decode_alias(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                const void* out, int B, int H, int H_kv, int M, int D,
+                                gqa_dtype_t in_dtype, gqa_dtype_t out_dtype) {
   const size_t ein = dtype_size(in_dtype), eout = dtype_size(out_dtype);
   const size_t qb = (size_t)B * H * D * ein, kvb = (size_t)B * H_kv * M * D * ein;
   const size_t ob = (size_t)B * H * D * eout;
   if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kvb) || overlaps(out, ob, v, kvb) ||
-      overlaps(out, ob, mask, (size_t)B * M) ||
-      (plan.workspace_bytes > 0 && overlaps(out, ob, workspace, plan.workspace_bytes)))
+      overlaps(out, ob, mask, (size_t)B * M))
     return GQA_ERR_ALIAS;
+  return GQA_OK;
+}
 
+// Launch a validated decode with its plan; `workspace` holds at least
+// plan.workspace_bytes bytes (counter area first) when that is nonzero.
+gqa_status_t launch_decode_plan(const gqa::DecodePlan& plan, const void* q, const void* k,
+                                const void* v, const uint8_t* mask, void* out, int B, int H,
+                                int H_kv, int M, int D, gqa_dtype_t in_dtype,
+                                gqa_dtype_t out_dtype, void* workspace, void* stream) {
   if (plan.wide) {
     // the group's heads as the query rows of a prefill over the same K/V:
     // q [B, H, 1, D] is [B, H_kv, g, D]; the [B, 1, M] mask serves every row
@@ -145,6 +124,116 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8
   }
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
+}
+
+// ---- the fixed scratch area of gqa_decode_noalloc ----------------------------
+// Each GPU holds its own copy of this array from the moment the library's
+// code is loaded on it until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): it uses the device address that hipGetSymbolAddress returns, kept
+// per device.
+static_assert(kScratchBytes > gqa::kCounterBytes, "scratch holds the counter area");
+
+__global__ void clear_words(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, or null when the
+// HIP runtime reports an error.  The first call on a device looks the address
+// up and clears the arrival counters with a small kernel on `stream`.
+void* scratch_for_current_device(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return;
+    const int words = (int)(gqa::kCounterBytes / 4);
+    hipLaunchKernelGGL(clear_words, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<unsigned*>(p), words);
+    if (hipGetLastError() != hipSuccess) return;
+    slot.ptr = p;
+  });
+  return slot.ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(gqa_status_t s) {
+  switch (s) {
+    case GQA_OK: return "success";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid shape (a dimension < 1, or sizes exceed the limits)";
+    case GQA_ERR_GROUP: return "H is not a multiple of H_kv";
+    case GQA_ERR_DTYPE: return "unsupported dtype combination";
+    case GQA_ERR_ALIGN: return "q/k/v/out/workspace must be 16-byte aligned";
+    case GQA_ERR_UNSUPPORTED:
+      return "unsupported size (need D <= 256, D*sizeof(dtype) % 16 == 0 and, paged, block_size % 16 == 0)";
+    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    case GQA_ERR_ALIAS: return "out overlaps an input or the workspace";
+    case GQA_ERR_SCRATCH:
+      return "the problem needs more scratch than gqa_decode_noalloc holds "
+             "(GQA_DECODE_NOALLOC_SCRATCH_BYTES); use gqa_decode with a workspace";
+  }
+  return "unknown status";
+}
+
+size_t gqa_decode_workspace_size(int B, int H, int H_kv, int M, int D) {
+  if (B < 1 || H < 1 || H_kv < 1 || M < 1 || D < 1 || H % H_kv != 0) return 0;
+  const long long kvrows = mul_checked({B, H_kv, M});
+  if (kvrows < 0 || kvrows >= INT_MAX || mul_checked({B, H}) >= INT_MAX) return 0;
+  return gqa::plan_decode(B, H, H_kv, M, D, false).workspace_bytes;
+}
+
+gqa_status_t gqa_decode(const void* q, const void* k, const void* v, const uint8_t* mask,
+                        void* out, int B, int H, int H_kv, int M, int D, gqa_dtype_t in_dtype,
+                        gqa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D, false);
+  if (plan.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return GQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return GQA_ERR_ALIGN;
+  }
+  st = check_decode_alias(q, k, v, mask, out, B, H, H_kv, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  if (plan.workspace_bytes > 0 && overlaps(out, (size_t)B * H * D * dtype_size(out_dtype),
+                                           workspace, plan.workspace_bytes))
+    return GQA_ERR_ALIAS;
+  return launch_decode_plan(plan, q, k, v, mask, out, B, H, H_kv, M, D, in_dtype, out_dtype,
+                            workspace, stream);
+}
+
+gqa_status_t gqa_decode_noalloc(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                void* out, int B, int H, int H_kv, int M, int D,
+                                gqa_dtype_t in_dtype, gqa_dtype_t out_dtype, void* stream) {
+  gqa_status_t st = check_common(q, k, v, out, B, H, H_kv, 1, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, H_kv, M, D, false);
+  if (plan.workspace_bytes > kScratchBytes) return GQA_ERR_SCRATCH;
+  st = check_decode_alias(q, k, v, mask, out, B, H, H_kv, M, D, in_dtype, out_dtype);
+  if (st != GQA_OK) return st;
+  void* ws = nullptr;
+  if (plan.workspace_bytes > 0) {
+    // the first call on this device finds the device's copy of the array
+    // and clears its counter area (on this stream, ahead of the decode)
+    ws = scratch_for_current_device(reinterpret_cast<hipStream_t>(stream));
+    if (ws == nullptr) return GQA_ERR_HIP;
+  }
+  return launch_decode_plan(plan, q, k, v, mask, out, B, H, H_kv, M, D, in_dtype, out_dtype, ws,
+                            stream);
 }
 
 size_t gqa_decode_paged_workspace_size(int B, int H, int H_kv, int max_blocks, int block_size,

@@ -65,6 +65,9 @@ extern "C" {
 /* Size of the counter area at the start of a decode workspace. */
 #define GQA_DECODE_COUNTER_BYTES 16384
 
+/* Size of the fixed per-GPU scratch area of gqa_decode_noalloc (16 MiB). */
+#define GQA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
 typedef enum {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                      */
@@ -76,7 +79,9 @@ typedef enum {
                               paged block_size that is not a multiple of 16  */
   GQA_ERR_WORKSPACE = 7,   /* decode workspace missing or too small           */
   GQA_ERR_HIP = 8,         /* the HIP runtime reported a launch error         */
-  GQA_ERR_ALIAS = 9        /* out overlaps an input or the workspace          */
+  GQA_ERR_ALIAS = 9,       /* out overlaps an input or the workspace          */
+  GQA_ERR_SCRATCH = 10     /* gqa_decode_noalloc: the problem needs more than
+                              GQA_DECODE_NOALLOC_SCRATCH_BYTES of scratch    */
 } gqa_status_t;
 
 typedef enum {
@@ -116,6 +121,31 @@ gqa_status_t gqa_decode(const void* q, const void* k, const void* v,
                         gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * Decode without allocation or workspace: for callers that cannot allocate
+ * device memory at call time (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same operation, arguments,
+ * layouts, results (bit for bit) and errors as gqa_decode, except that the
+ * key-split partials and arrival counters live in a fixed scratch area that
+ * the library holds on each GPU it runs on, from the first call on that GPU
+ * until the process ends: GQA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) of
+ * device memory.  No call allocates or frees anything.
+ *   - Problems whose gqa_decode_workspace_size(...) exceeds that size are
+ *     rejected with GQA_ERR_SCRATCH before any HIP call.
+ *   - The first call on a GPU looks up the scratch area and clears its
+ *     counters with a small kernel on `stream`, ahead of the decode.
+ *   - Every call on one GPU uses the same scratch area, and each call leaves
+ *     the counters zero for the next one.  Calls that may overlap on one GPU
+ *     (different streams, or graphs replayed concurrently) race on it and
+ *     give wrong results: serialise them, or use gqa_decode with one
+ *     workspace per stream.
+ */
+gqa_status_t gqa_decode_noalloc(const void* q, const void* k, const void* v,
+                                const uint8_t* mask, void* out,
+                                int B, int H, int H_kv, int M, int D,
+                                gqa_dtype_t in_dtype, gqa_dtype_t out_dtype,
+                                void* stream);
 
 /*
  * Bytes of decode workspace for these sizes (independent of dtype and of

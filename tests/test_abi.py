@@ -14,7 +14,7 @@ import grouped_query_attention_fwd_amd as gqa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa.h")
 
-OK, NULL, SHAPE, GROUP, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(10)
+OK, NULL, SHAPE, GROUP, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS, SCRATCH = range(11)
 F32, BF16, F16 = 0, 1, 2
 
 # fake, 16-byte aligned, non-overlapping "device" addresses: never dereferenced
@@ -34,7 +34,8 @@ def lib():
 
 def test_exports_match_header(lib):
     names = declared_functions()
-    assert names == ["gqa_decode", "gqa_decode_paged", "gqa_decode_paged_workspace_size",
+    assert names == ["gqa_decode", "gqa_decode_noalloc", "gqa_decode_paged",
+                     "gqa_decode_paged_workspace_size",
                      "gqa_decode_workspace_size", "gqa_prefill", "gqa_prefill_band",
                      "gqa_status_string"]
     for n in names:
@@ -47,7 +48,7 @@ def test_exports_match_header(lib):
 
 
 def test_status_strings(lib):
-    for code in range(10):
+    for code in range(11):
         s = gqa.status_string(code)
         assert s and s != "unknown status"
     assert gqa.status_string(123) == "unknown status"
@@ -187,8 +188,11 @@ def test_paged_workspace_layout(lib):
 def test_counter_area_constant_matches_header():
     import re
     with open(os.path.join(ROOT, "include", "gqa.h")) as fh:
-        m = re.search(r"#define GQA_DECODE_COUNTER_BYTES (\d+)", fh.read())
+        src = fh.read()
+    m = re.search(r"#define GQA_DECODE_COUNTER_BYTES (\d+)", src)
     assert m and int(m.group(1)) == gqa.DECODE_COUNTER_BYTES
+    m = re.search(r"#define GQA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == gqa.DECODE_NOALLOC_SCRATCH_BYTES
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
@@ -201,3 +205,25 @@ def test_binding_fails_loudly_without_gpu_tensors():
     bt = torch.zeros(1, 1, dtype=torch.int32)
     with pytest.raises(ValueError):
         gqa.decode_paged(q, q[:, :2], q[:, :2], bt, bt[0])
+
+
+def noalloc(lib, q=Q, k=K, v=V, mask=None, out=O, B=2, H=8, H_kv=2, M=300, D=128,
+            tin=BF16, tout=BF16):
+    return lib.gqa_decode_noalloc(q, k, v, mask, out, B, H, H_kv, M, D, tin, tout, None)
+
+
+def test_noalloc_validation(lib):
+    """gqa_decode_noalloc checks like gqa_decode, and rejects a problem whose
+    workspace would exceed the fixed scratch area, all before any HIP call."""
+    assert noalloc(lib, q=None) == NULL
+    assert noalloc(lib, B=0) == SHAPE
+    assert noalloc(lib, H=9, H_kv=2) == GROUP
+    assert noalloc(lib, tin=BF16, tout=F16) == DTYPE
+    assert noalloc(lib, D=100) == UNSUP
+    assert noalloc(lib, q=Q + 8) == ALIGN
+    assert noalloc(lib, out=Q) == ALIAS
+    big = (1, 256, 1, 16384, 256)
+    assert gqa.decode_workspace_size(*big) > gqa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, B=big[0], H=big[1], H_kv=big[2], M=big[3], D=big[4]) == SCRATCH
+    # a problem that fits needs a GPU (it would launch): not called here
+    assert 0 < gqa.decode_workspace_size(16, 32, 8, 4096, 128) <= gqa.DECODE_NOALLOC_SCRATCH_BYTES
