@@ -50,13 +50,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
     "decode_paged": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
+    "decode_wide": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "prefill.hip"),
     "prefill": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "prefill.hip"),
 }
-# the kernel one call launches (the decode merges its key splits inside the kernel)
+# the kernel one call launches (the decode merges its key splits inside the
+# kernel); a decode with more than WIDE_MIN_G heads per KV head runs as a
+# prefill over the group's heads plus a split merge (the library's plan)
+WIDE_MIN_G = 32
 KERNEL_NAMES = {"decode": "decode_kernel", "decode_paged": "decode_kernel",
-                "prefill": "prefill_kernel"}
+                "decode_wide": "prefill_kernel", "prefill": "prefill_kernel"}
 KERNEL_PATTERNS = {"decode": ("decode_kernel",), "decode_paged": ("decode_kernel",),
+                   "decode_wide": ("prefill_kernel", "prefill_merge_kernel"),
                    "prefill": ("prefill_kernel",)}
+DECODE_KINDS = ("decode", "decode_paged", "decode_wide")
 
 
 def log(*a):
@@ -98,6 +104,18 @@ def source_sha(kind):
 
 
 # ----------------------------------------------------------------- workloads
+def kind_of(name):
+    """decode, decode_paged, decode_wide or prefill: which kernels a call of
+    the named workload launches."""
+    import workloads
+    if name.startswith("decode_paged"):
+        return "decode_paged"
+    w = workloads.by_name(name)
+    if w.kind == "decode" and w.H // w.H_kv > WIDE_MIN_G:
+        return "decode_wide"
+    return w.kind
+
+
 def setup_paged(name, torch, copies=1):
     import workloads
     from grouped_query_attention_fwd_amd import accounting
@@ -124,7 +142,7 @@ def setup(name, torch, copies=1):
         else:   # distinct buffers with the same contents
             sets.append([t.cuda().clone() if t is not None else None for t in (q, k, v, mask)])
     elt = 4 if w.dtype == "fp32" else 2
-    info = {"w": w, "kind": w.kind, "cpu": (q, k, v, mask, causal), "sets": sets}
+    info = {"w": w, "kind": kind_of(name), "cpu": (q, k, v, mask, causal), "sets": sets}
     if w.kind == "decode":
         info["units"] = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, elt)
     elif w.band is not None:
@@ -266,7 +284,7 @@ def result_for(info, timing):
     # single call, reported as launch_us, adds the events' own packets)
     avg_s = timing["ms_per_step"] * 1e-3
     whole_s = timing["ms_per_step"] * 1e-3
-    if kind in ("decode", "decode_paged"):
+    if kind in DECODE_KINDS:
         achieved = info["units"] / avg_s / 1e9
         value = info["units"] / whole_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -315,13 +333,11 @@ def cpu_baseline(info, budget_s=12.0, max_rows=None):
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:   # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
     q, k, v, mask, causal = info["cpu"]
     w = info["w"]
+    if w.kind == "prefill":
+        return cpu_baseline_prefill(info, budget_s, threads)
     done_units, t_used, rows = 0, 0.0, 0
     while t_used < budget_s and (max_rows is None or rows < max_rows):
         b = rows % w.B
@@ -341,6 +357,144 @@ def cpu_baseline(info, budget_s=12.0, max_rows=None):
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{rows} batch rows of {w.name} ({rows / w.B:.2f} x the workload; "
                       f"{t_used:.1f} s of fp64 numpy on the host)"}
+
+
+def cpu_baseline_prefill(info, budget_s, threads, rows_per_call=256):
+    """The fp64 oracle on sampled query rows of a prefill workload: for one
+    batch row at a time, rows_per_call query rows spread evenly over N (a
+    different offset each call), with their band or causal visibility given
+    to the oracle as an explicit [1, rows, M] mask; repeated over batch rows
+    until about budget_s seconds.  Throughput counts 4 D flop per visible
+    (query, key) pair and head, as for the GPU."""
+    import numpy as np
+
+    import oracle
+    q, k, v, mask, causal = info["cpu"]
+    w = info["w"]
+    band = w.band if w.band is not None else (0, -1, 0 if causal else -1)
+    q_off, wl, wr = band
+    step = max(1, w.N // rows_per_call)
+    flops, t_used, calls = 0, 0.0, 0
+    while t_used < budget_s:
+        b = calls % w.B
+        rows = np.arange((calls // w.B) % step, w.N, step)[:rows_per_call]
+        pos = rows[:, None] + q_off
+        j = np.arange(w.M)[None, :]
+        vis = np.ones((len(rows), w.M), dtype=bool)
+        if wl >= 0:
+            vis &= j >= pos - wl
+        if wr >= 0:
+            vis &= j <= pos + wr
+        if mask is not None:
+            vis &= mask[b, rows].numpy()
+        qb = q[b:b + 1, :, rows].float().numpy().astype(np.float64)
+        kb = k[b:b + 1].float().numpy().astype(np.float64)
+        vb = v[b:b + 1].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.gqa(qb, kb, vb, vis[None])
+        t_used += time.perf_counter() - t0
+        flops += 4 * w.D * w.H * int(vis.sum())
+        calls += 1
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} calls of {rows_per_call} query rows x all {w.H} heads of one "
+                      f"batch row of {w.name} ({flops / info['units']:.5f} x the workload's "
+                      f"flops; {t_used:.1f} s of fp64 numpy on the host)"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:   # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+# ------------------------------------------------------ calibration probes
+def hbm_read_probe(torch, steps=30):
+    """The read rate plain streaming kernels reach on this GPU, for
+    comparison with the decode: over 268,435,456 bytes (four rotating copies,
+    so that no call finds its data in the 256 MB last-level cache) and over
+    2 GiB, the read-only kernels of libgqa_probe.so (one contiguous slab per
+    workgroup, or all workgroups sweeping together; 256 to 1024 workgroups;
+    8 or 16 16-byte loads in flight per thread; normal or non-temporal
+    loads), and torch's sum of a bf16 tensor for reference.  Times are HIP
+    events around `steps` back-to-back calls on the launching stream."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "grouped_query_attention_fwd_amd", "libgqa_probe.so"))
+    lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gqa_probe_read.restype = ctypes.c_int
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for nbytes, copies in ((268435456, 4), (2 << 30, 1)):
+        bufs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+        variants = [("torch_sum", None)]
+        for mode in (0, 1):
+            for wgs in (256, 512, 1024):
+                for unroll in (8, 16):
+                    for nt in (0, 1):
+                        variants.append((f"{'slabs' if mode == 0 else 'sweep'}_wg{wgs}_u{unroll}"
+                                         f"{'_nt' if nt else ''}", (wgs, mode, unroll, nt)))
+        rows = []
+        for name, cfg in variants:
+            def call(i, cfg=cfg):
+                b = bufs[i % copies]
+                if cfg is None:
+                    b.sum(dtype=torch.float32)
+                else:
+                    rc = lib.gqa_probe_read(b.data_ptr(), nbytes, cfg[0], cfg[1], cfg[2], cfg[3],
+                                            sink.data_ptr(), stream)
+                    if rc != 0:
+                        raise RuntimeError(f"read probe {name}: status {rc}")
+            for i in range(8):
+                call(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                call(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            rows.append({"variant": name, "us_per_call": round(us, 2),
+                         "GB_per_s": round(nbytes / us / 1e3, 1)})
+        best = max((r_ for r_ in rows if r_["variant"] != "torch_sum"), key=lambda r_: r_["GB_per_s"])
+        res[str(nbytes)] = {"copies": copies, "best": best, "variants": rows}
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+def decode_size_sweep(torch, steps=30, warmup=5):
+    """The Mistral-7B-shaped decode (B16, 32 / 8 heads, D 128, bf16) over
+    M = 1024 ... 32768 cached keys, timed like the benchmark; a least-squares
+    line t = t0 + bytes / rate through the points splits each call into a
+    fixed cost t0 and a streaming rate."""
+    import workloads
+    from grouped_query_attention_fwd_amd import accounting
+    pts = []
+    for M in (1024, 2048, 4096, 8192, 16384, 32768):
+        w = workloads.Workload(f"decode_mistral7b_m{M}", 2, 16, 32, 8, 1, M, 128, "bf16")
+        q, k, v, mask, causal = workloads.make_inputs(w)
+        kv = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, 2)
+        copies = max(1, -(-(640 << 20) // kv))
+        sets = [[t.cuda().clone() for t in (q, k, v)] for _ in range(copies)]
+        info = {"w": w, "kind": "decode", "sets": [s_ + [None] for s_ in sets], "cpu": None}
+        timing = time_workload(info, steps, warmup, torch)
+        us = timing["ms_per_step"] * 1e3
+        pts.append({"M": M, "kv_bytes": kv, "us_per_launch": round(us, 2),
+                    "GB_per_s": round(kv / us / 1e3, 1)})
+        del sets, info
+        torch.cuda.empty_cache()
+    import numpy as np
+    x = np.array([p_["kv_bytes"] for p_ in pts], dtype=np.float64)
+    y = np.array([p_["us_per_launch"] for p_ in pts], dtype=np.float64)
+    slope, t0 = np.polyfit(x, y, 1)
+    return {"points": pts, "fit": {"fixed_us": round(float(t0), 2),
+                                   "stream_GB_per_s": round(1e-3 / float(slope), 1)}}
 
 
 # ---------------------------------------------------------- counter support
@@ -363,9 +517,7 @@ def summarize_pmc(workload, fetch_dir, write_dir):
     (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled
     by what it reads for the 1 GiB copy in the same run (factor = true bytes
     / counted bytes), then summed over the kernels of one call."""
-    import workloads
-    kind = ("decode_paged" if workload.startswith("decode_paged")
-            else workloads.by_name(workload).kind)
+    kind = kind_of(workload)
 
     def load(d, counter):
         rows = []
@@ -406,6 +558,10 @@ def main():
     ap.add_argument("--profile-run", default=None)
     ap.add_argument("--summarize-pmc", nargs=3, default=None,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--hbm-read-probe", action="store_true",
+                    help="time plain torch streaming reads over 268 MB and 2 GiB")
+    ap.add_argument("--decode-size-sweep", action="store_true",
+                    help="time the Mistral-7B-shaped decode over M = 1024 ... 32768")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -435,6 +591,12 @@ def main():
     if args.profile_run:
         profile_run(args.profile_run)
         return 0
+    if args.hbm_read_probe:
+        print(json.dumps({"hbm_read_probe": hbm_read_probe(torch)}), flush=True)
+        return 0
+    if args.decode_size_sweep:
+        print(json.dumps({"decode_size_sweep": decode_size_sweep(torch)}), flush=True)
+        return 0
 
     primary = args.only or "decode_mistral7b_m4096"
     names = [primary]
@@ -447,6 +609,8 @@ def main():
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}
     primary_info = None
+    # the oracle timed beside the prefill half of the metric as well
+    cpu_side = {"prefill_causal_n4096"} if not args.no_cpu_baseline else set()
     for name in names:
         log(f"[bench] setting up {name}")
         info = setup(name, torch, copies=copies.get(name, 1))
@@ -461,6 +625,9 @@ def main():
         if name == primary:
             primary_info = info
         else:
+            if name in cpu_side:
+                log(f"[bench] timing the fp64 oracle on a CPU sample of {name}")
+                results[name]["cpu_baseline"] = cpu_baseline(info, budget_s=10.0)
             del info
             torch.cuda.empty_cache()
 
@@ -479,7 +646,9 @@ def main():
             r = result_for(info, timing)
             sweep.append({"g": w.H // w.H_kv, "H_kv": w.H_kv, "value": r["value"],
                           "unit": r["unit"], "us_per_launch": r["roofline"]["duration_us"],
-                          "frac": r["roofline"]["frac"], "kv_bytes": kv})
+                          "frac": r["roofline"]["frac"], "kv_bytes": kv,
+                          "kernel": r["roofline"]["kernel"],
+                          "traffic": r["roofline"]["traffic"]})
             del info
             torch.cuda.empty_cache()
 
@@ -510,7 +679,8 @@ def main():
     sec = [results[n] for n in names if n != primary]
     if sec:
         line["secondary"] = [{k: r[k] for k in ("workload", "value", "unit", "ms_per_step",
-                                                "launch_us", "graph_us_per_launch", "roofline")}
+                                                "launch_us", "graph_us_per_launch", "roofline",
+                                                "cpu_baseline") if k in r}
                              for r in sec]
     if sweep:
         line["group_sweep"] = {"workload": "decode B16 H64 M4096 D128 bf16, H_kv = 64 / g",

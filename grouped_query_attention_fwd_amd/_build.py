@@ -13,6 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+PROBE_LIB = os.path.join(PKG, "libgqa_probe.so")
 SOURCES = ["gqa_api.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
@@ -53,6 +54,11 @@ def build(verbose: bool = False) -> str:
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
                       f"-Wl,--version-script={vers}"]))
     os.replace(tmp, LIB)
+    # the HBM read-rate probe the benchmark uses for calibration: its own
+    # library, not part of the attention path
+    ptmp = PROBE_LIB + ".tmp"
+    outs.append(_run([HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, "read_probe.hip"), "-o", ptmp]))
+    os.replace(ptmp, PROBE_LIB)
     if verbose:
         for o in outs:
             if o.strip():

@@ -19,7 +19,8 @@
 // (contiguous rows, or one block-table entry of a paged cache, in which case
 // each sequence's own length ends its key range).  Per chunk a wave
 //   1. loads K rows straight into MFMA operand registers (16 bytes per lane)
-//      and V rows with coalesced 16-byte loads, all issued up front with
+//      and V rows with coalesced 16-byte loads, non-temporal (each byte is
+//      read once per call; the hint measured 10-12 % faster), all issued up front with
 //      clamped (always valid) addresses so nothing waits on a branch, one
 //      chunk ahead of the math (two register buffers used in turn; a paged
 //      cache's block-table entries are read one chunk further ahead);
@@ -67,12 +68,20 @@ constexpr int kRoundKeys = 256;  // keys_per_split is a multiple of this
 #ifndef GQA_DECODE_WIDE_TARGET_WGS
 #define GQA_DECODE_WIDE_TARGET_WGS 256
 #endif
+// The paged form launches this many workgroups for fewer units (two rounds
+// of 256 CUs: with mixed lengths, shorter pieces even out the CUs' work;
+// measured 33.4 against 35.7 us on the mixed-length Mistral-shaped batch).
+// Near-equal lengths use only kPagedEvenWGs of them (below).
 #ifndef GQA_DECODE_PAGED_TARGET_WGS
-#define GQA_DECODE_PAGED_TARGET_WGS 256
+#define GQA_DECODE_PAGED_TARGET_WGS 512
 #endif
 static_assert(GQA_DECODE_TARGET_WGS <= kMaxCounters && GQA_DECODE_PAGED_TARGET_WGS <= kMaxCounters,
               "a split plan needs fewer units than the counter area holds");
 static_assert(GQA_DECODE_PAGED_TARGET_WGS % 8 == 0, "the piece grid is a multiple of the XCD count");
+// Pieces planned for near-equal lengths: one per CU.  Cutting them for two
+// rounds of workgroups only adds restarts and merges (the full-length
+// batch: 49.5 against 48.2 us).
+constexpr int kPagedEvenWGs = 256;
 // 1: a paged decode that splits keys cuts them into pieces balanced over
 // the actual sequence lengths, planned in the kernel (GQA_DECODE_PAGED_
 // TARGET_WGS workgroups); 0: the static split plan, sized for the longest
@@ -234,7 +243,8 @@ struct Piece {
 // ceil(N / (G - U)) (N = sum_u n_u, U units; the upper end always fits,
 // since sum_u S_u <= N / P + U).  Unit u's groups are then cut into S_u
 // near-equal pieces.  Near-equal lengths skip the search: each unit is one
-// piece (256 units or more) or floor(G / U) pieces.  Pieces are numbered unit by unit, units in
+// piece (256 units or more) or floor(256 / U) pieces, one wave of
+// workgroups.  Pieces are numbered unit by unit, units in
 // order, and spread over the XCDs (below); workgroups left over have none.
 // All units of batch row b share its length, so the sums run over batch
 // rows, one wave reduction per 64 rows (kv_len is re-read from cache in
@@ -270,10 +280,11 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
   // Near-equal lengths (longest within 25 % of the mean) need no search.
   // With more units than one wave of workgroups, one piece per unit:
   // cutting them would only add a second round of workgroups and merges.
-  // Otherwise floor(G / U) pieces per unit, P = ceil(nmax / that), which
-  // fits G and is the search's answer when all lengths are equal.
+  // Otherwise floor(256 / U) pieces per unit (one wave of workgroups; the
+  // rest of the G find no piece and return), P = ceil(nmax / that), which
+  // fits G.
   if (4LL * nmax * U <= 5LL * N) {
-    const int k = U >= 256 ? 1 : G / U;
+    const int k = U >= kPagedEvenWGs ? 1 : min(G, kPagedEvenWGs) / U;
     lo = hi = max(1, (nmax + k - 1) / k);
   }
   while (lo < hi) {
@@ -323,8 +334,11 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
 
 // EXACT: D == DP, so no column of a row needs masking.  MASKED: a mask is
 // given.  PAGED: K/V rows are found through a block table and each sequence
-// has its own length.
-template <int ET, int DP, bool EXACT, bool MASKED, bool PAGED, bool OUTF32>
+// has its own length.  NT: K/V loads carry the non-temporal hint; off when
+// a unit's rows are read again by the unit of the group's next head chunk
+// (the hint would evict them from L2 before that second read: g = 32 took
+// 23.2 against 21.5 us with it).
+template <int ET, int DP, bool EXACT, bool MASKED, bool PAGED, bool OUTF32, bool NT>
 __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs a) {
   constexpr bool H16 = ET != kF32;  // 16-bit elements: bf16 or fp16
   using C = DecCfg<H16, DP>;
@@ -458,6 +472,13 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     }
     return tb;
   };
+  auto ldkv = [](const char* p) -> u32x4 {
+    if constexpr (NT) {
+      return ld16_stream(p);
+    } else {
+      return ld16(p);
+    }
+  };
   auto load_chunk = [&](int base, const Tab& tb) {
     Chunk ch;
     int g16[C::NKB];
@@ -475,10 +496,10 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       for (int u = 0; u < C::QCH; ++u) {
         const int d0 = H16 ? (32 * u + 8 * qg) : (16 * u + 4 * qg);
         if constexpr (EXACT) {
-          ch.k[kb][u] = ld16(krow + (size_t)d0 * C::ELT);
+          ch.k[kb][u] = ldkv(krow + (size_t)d0 * C::ELT);
         } else {
           const bool dv = d0 < D;
-          ch.k[kb][u] = ld16(krow + (size_t)(dv ? d0 : 0) * C::ELT);  // zeroed at use
+          ch.k[kb][u] = ldkv(krow + (size_t)(dv ? d0 : 0) * C::ELT);  // zeroed at use
         }
       }
     }
@@ -494,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       const int d0 = chunk * (16 / C::ELT);
       const bool ok = key < k_end && (EXACT || d0 < D);
       const size_t roff = goff[grp] + (size_t)(min(key, klast) - g16[grp]) * D * C::ELT;
-      ch.v[it] = ld16(vp + roff + (size_t)(ok ? d0 : 0) * C::ELT);  // zeroed at use
+      ch.v[it] = ldkv(vp + roff + (size_t)(ok ? d0 : 0) * C::ELT);  // zeroed at use
     }
     return ch;
   };
@@ -740,18 +761,29 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   }
 }
 
-template <int ET, int DP, bool EXACT, bool OUTF32>
-hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
+template <int ET, int DP, bool EXACT, bool OUTF32, bool NT>
+hipError_t launch_nt(const DecodeArgs& a, hipStream_t stream) {
   const int units = a.B * a.H_kv * a.head_chunks;
   const dim3 grid = a.pieces > 0 ? dim3(a.pieces) : fold_grid(units, (unsigned)a.splits);
   if (a.block_table) {  // the paged form takes no mask
-    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, true, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, true, OUTF32, NT>), grid, dim3(kThreads), 0, stream, a);
   } else if (a.mask) {
-    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, true, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, true, false, OUTF32, NT>), grid, dim3(kThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, false, OUTF32>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<ET, DP, EXACT, false, false, OUTF32, NT>), grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+// Non-temporal K/V loads unless the group's head chunks re-read the rows
+// (fp32 inputs always take them: one kernel instance less per shape, and the
+// hint only changes the speed).
+template <int ET, int DP, bool EXACT, bool OUTF32>
+hipError_t launch_dp(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (ET != kF32) {
+    if (a.head_chunks > 1) return launch_nt<ET, DP, EXACT, OUTF32, false>(a, stream);
+  }
+  return launch_nt<ET, DP, EXACT, OUTF32, true>(a, stream);
 }
 
 template <int ET, int DP, bool OUTF32>

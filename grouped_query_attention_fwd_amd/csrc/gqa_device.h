@@ -141,6 +141,14 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// 16-byte global load with the non-temporal hint (global_load_dwordx4 ...
+// nt): for data read once per call, such as a decode's K/V stream.  Measured
+// on MI355X: plain streaming reads of 268 MB and 2 GiB reach 6.9 and 7.2 TB/s
+// with the hint against 6.2 and 6.4 TB/s without it.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ u32x4 sel16(bool keep, u32x4 v) {

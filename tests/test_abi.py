@@ -170,17 +170,18 @@ def test_workspace_size_rules(lib):
 
 def test_paged_workspace_layout(lib):
     """Paged workspace: the counter area, then one [16][D + 4] fp32 partial
-    per piece of the length-balanced plan.  The plan launches 256 pieces
-    for fewer than 256 (batch row, KV head, head chunk) units, else two per
+    per piece of the length-balanced plan.  The plan launches 512 pieces
+    for fewer than 512 (batch row, KV head, head chunk) units, else two per
     unit rounded up to a multiple of 8; caches of at most 256 key slots are
     not split (no workspace)."""
     f = lib.gqa_decode_paged_workspace_size
     part = 16 * (128 + 4) * 4
     nc = gqa.DECODE_COUNTER_BYTES
-    assert f(16, 32, 8, 256, 16, 128) == nc + 256 * part       # 128 units
+    assert f(16, 32, 8, 256, 16, 128) == nc + 512 * part       # 128 units
     assert f(64, 32, 8, 256, 16, 128) == nc + 1024 * part      # 512 units
-    assert f(31, 8, 1, 64, 16, 128) == nc + 256 * part         # 31 units
-    assert f(129, 6, 2, 64, 16, 128) == nc + 520 * part        # 258 units -> 2 * 258 rounded to 520
+    assert f(31, 8, 1, 64, 16, 128) == nc + 512 * part         # 31 units
+    assert f(129, 6, 2, 64, 16, 128) == nc + 512 * part        # 258 units
+    assert f(260, 6, 2, 64, 16, 128) == nc + 1040 * part       # 520 units -> 2 * 520
     assert f(16, 32, 8, 16, 16, 128) == 0                      # 256 key slots: no split
     assert f(4096, 8, 1, 64, 16, 128) == 0                     # 4096 units: static plan
 
