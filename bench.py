@@ -497,6 +497,79 @@ def decode_size_sweep(torch, steps=30, warmup=5):
                                    "stream_GB_per_s": round(1e-3 / float(slope), 1)}}
 
 
+def decode_trace(name, torch, reps=20):
+    """Per-workgroup phase budget of one decode workload from the timing
+    build (libgqa_trace.so, `python -m grouped_query_attention_fwd_amd._build
+    --trace`): each workgroup records wall-clock ticks at its start, when its
+    waves have finished their keys, after its arrival ticket and at its end,
+    plus its XCD and CU.  Per call: how far apart the workgroups start, when
+    the key phase ends (median / slowest workgroup, per XCD), what the split
+    merge adds, and the whole span; medians over `reps` calls."""
+    import ctypes
+
+    import numpy as np
+
+    import grouped_query_attention_fwd_amd as gqa
+    path = os.path.join(ROOT, "grouped_query_attention_fwd_amd", "libgqa_trace.so")
+    lib = gqa.load_library(path)
+    lib.gqa_debug_decode_trace.argtypes = [ctypes.c_void_p]
+    lib.gqa_debug_wall_clock_khz.restype = ctypes.c_int
+    khz = lib.gqa_debug_wall_clock_khz()
+    if khz <= 0:
+        raise RuntimeError("wall clock rate unavailable")
+    records = 8192
+    buf = torch.zeros(records * 8, dtype=torch.int64, device="cuda")
+    lib.gqa_debug_decode_trace(ctypes.c_void_p(buf.data_ptr()))
+    copies = 4 if name.startswith(("decode_mistral", "decode_paged")) else 1
+    info = setup(name, torch, copies=copies)
+    call = make_call(info, torch)
+    for i in range(10):
+        call(i)
+    torch.cuda.synchronize()
+    per_call = []
+    for r in range(reps):
+        buf.zero_()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(r)
+        e1.record()
+        torch.cuda.synchronize()
+        rec = buf.view(records, 8).cpu().numpy()
+        rec = rec[rec[:, 0] != 0]
+        us = lambda t: t * 1e3 / khz   # noqa: E731 - ticks to microseconds
+        t0 = rec[:, 0].min()
+        start = us(rec[:, 0] - t0)
+        keys = us(rec[:, 1] - t0)
+        end = us(rec[:, 3] - t0)
+        xcd = (rec[:, 4] >> 16) & 0xF
+        merged = rec[:, 7] == 1
+        split = rec[:, 2] != 0
+        per_xcd = [float(np.median(keys[xcd == x])) for x in range(8) if (xcd == x).any()]
+        per_call.append({
+            "event_us": e0.elapsed_time(e1) * 1e3,
+            "workgroups": int(len(rec)),
+            "start_spread_us": float(start.max()),
+            "keys_done_median_us": float(np.median(keys)),
+            "keys_done_max_us": float(keys.max()),
+            "key_phase_median_us": float(np.median(keys - start)),
+            "xcd_keys_done_median_min_us": min(per_xcd),
+            "xcd_keys_done_median_max_us": max(per_xcd),
+            "ticket_after_keys_median_us": (float(np.median(us(rec[split, 2] - rec[split, 1])))
+                                            if split.any() else 0.0),
+            "merge_us_median": (float(np.median(us(rec[merged, 3] - rec[merged, 2])))
+                                if merged.any() else 0.0),
+            "span_us": float(end.max()),
+            "last_end_minus_last_keys_us": float(end.max() - keys.max()),
+        })
+    lib.gqa_debug_decode_trace(None)
+    keys_ = per_call[0].keys()
+    summary = {k: round(float(np.median([c[k] for c in per_call])), 2) for k in keys_}
+    return {"workload": name, "wall_clock_khz": khz, "calls": reps,
+            "median_over_calls": summary}
+
+
 # ---------------------------------------------------------- counter support
 def profile_run(name, steps=3):
     import torch
@@ -562,6 +635,8 @@ def main():
                     help="time plain torch streaming reads over 268 MB and 2 GiB")
     ap.add_argument("--decode-size-sweep", action="store_true",
                     help="time the Mistral-7B-shaped decode over M = 1024 ... 32768")
+    ap.add_argument("--decode-trace", default=None, metavar="WORKLOAD",
+                    help="per-workgroup phase budget of a decode workload (timing build)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -586,6 +661,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     import grouped_query_attention_fwd_amd as gqa
+    if args.decode_trace:
+        print(json.dumps({"decode_trace": decode_trace(args.decode_trace, torch)}), flush=True)
+        return 0
     gqa.load_library()   # fail loudly if the HIP library is missing
 
     if args.profile_run:

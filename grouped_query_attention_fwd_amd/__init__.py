@@ -66,16 +66,21 @@ def library_path() -> str:
     return _LIB_PATH
 
 
-def load_library():
-    """Load libgqa.so once; raise if it has not been built."""
+def load_library(path=None):
+    """Load libgqa.so once; raise if it has not been built.  `path` loads
+    another build of the same library instead (the benchmark's timing build),
+    and only before the first load."""
     global _lib
     if _lib is not None:
+        if path is not None and path != _lib._name:
+            raise RuntimeError(f"{_lib._name} is already loaded")
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = _LIB_PATH if path is None else path
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"HIP library not built: {_LIB_PATH} is missing "
+            f"HIP library not built: {path} is missing "
             "(build it with `python -m grouped_query_attention_fwd_amd._build`)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.gqa_decode.restype = i

@@ -1,18 +1,27 @@
 """Build step for libgqa.so (hipcc, gfx950).  Run as a module or through the
-repository's build() entry point; it always recompiles."""
+repository's build() entry point; it always recompiles.
+
+    python -m grouped_query_attention_fwd_amd._build [-v]
+    python -m grouped_query_attention_fwd_amd._build --trace
+
+--trace builds libgqa_trace.so instead: the same library with the decode's
+per-workgroup timing records compiled in (GQA_DECODE_TRACE), for
+`bench.py --decode-trace`.  It is never loaded by the attention path."""
 
 from __future__ import annotations
 
 import concurrent.futures
 import os
-import subprocess
 import sys
+
+import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
+TRACE_LIB = os.path.join(PKG, "libgqa_trace.so")
 PROBE_LIB = os.path.join(PKG, "libgqa_probe.so")
 SOURCES = ["gqa_api.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
@@ -37,34 +46,45 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def _library(lib, build_dir, defines):
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         outs = list(ex.map(_run, cmds))
-    vers = os.path.join(BUILD, "exports.map")
+    vers = os.path.join(build_dir, "exports.map")
     with open(vers, "w") as f:
         f.write("{ global: gqa_*; local: *; };\n")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
                       f"-Wl,--version-script={vers}"]))
-    os.replace(tmp, LIB)
-    # the HBM read-rate probe the benchmark uses for calibration: its own
-    # library, not part of the attention path
-    ptmp = PROBE_LIB + ".tmp"
-    outs.append(_run([HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, "read_probe.hip"), "-o", ptmp]))
-    os.replace(ptmp, PROBE_LIB)
+    os.replace(tmp, lib)
+    return outs
+
+
+def build(verbose: bool = False, trace: bool = False) -> str:
+    if trace:
+        outs = _library(TRACE_LIB, os.path.join(BUILD, "trace"), ["-DGQA_DECODE_TRACE=1"])
+        lib = TRACE_LIB
+    else:
+        outs = _library(LIB, BUILD, [])
+        # the HBM read-rate probe the benchmark uses for calibration: its own
+        # library, not part of the attention path
+        ptmp = PROBE_LIB + ".tmp"
+        outs.append(_run([HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, "read_probe.hip"),
+                          "-o", ptmp]))
+        os.replace(ptmp, PROBE_LIB)
+        lib = LIB
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

@@ -46,6 +46,15 @@
 namespace gqa {
 namespace {
 
+// 1: the timing build.  Every workgroup writes one record to a.trace:
+// wall-clock ticks at its start, when all its waves have finished their
+// keys, after its arrival ticket and at its end, where it ran (XCD, shader
+// engine, CU), its unit and split, and whether it merged.  Off in the
+// library proper (no code at all).
+#ifndef GQA_DECODE_TRACE
+#define GQA_DECODE_TRACE 0
+#endif
+
 #ifndef GQA_DECODE_WAVES
 #define GQA_DECODE_WAVES 4
 #endif
@@ -343,6 +352,26 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   constexpr bool H16 = ET != kF32;  // 16-bit elements: bf16 or fp16
   using C = DecCfg<H16, DP>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
+#if GQA_DECODE_TRACE
+  const unsigned long long tr_start = (unsigned long long)wall_clock64();
+  unsigned long long tr_keys = 0, tr_ticket = 0;
+  const unsigned tr_wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  auto trace_out = [&](int merged) {
+    if (threadIdx.x == 0 && a.trace != nullptr && tr_wg < (unsigned)kTraceRecords) {
+      const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);   // XCC_ID[3:0]
+      const unsigned hw = __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 4);    // HW_ID[15:0]
+      unsigned long long* r = a.trace + (size_t)tr_wg * 8;
+      r[0] = tr_start;
+      r[1] = tr_keys;
+      r[2] = tr_ticket;
+      r[3] = (unsigned long long)wall_clock64();
+      r[4] = ((unsigned long long)xcc << 16) | hw;   // hw: CU in bits 11:8, SE in 14:13
+      r[5] = (unsigned long long)blockIdx.x;
+      r[6] = (unsigned long long)blockIdx.y;
+      r[7] = (unsigned long long)merged;
+    }
+  };
+#endif
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -687,6 +716,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   // ---- merge the waves through LDS -----------------------------------
   const float l_tot = rows_sum(l_run);
   __syncthreads();  // all waves are done with their V areas
+#if GQA_DECODE_TRACE
+  tr_keys = (unsigned long long)wall_clock64();
+#endif
   float* cacc = reinterpret_cast<float*>(smem_raw);              // [4][16][DP]
   float* cm = cacc + kWaves * 16 * DP;                           // [4][16]
   float* cl = cm + kWaves * 16;                                  // [4][16]
@@ -733,7 +765,12 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       if (d == 0) st_dev2(prs, ro, f32x2{mx, L});
     }
   }
-  if (single) return;
+  if (single) {
+#if GQA_DECODE_TRACE
+    trace_out(0);
+#endif
+    return;
+  }
 
   // ---- the last split of the unit to arrive merges all of them -----------
   // Partials are stored and loaded with device-scope accesses, which bypass
@@ -750,6 +787,10 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     s_last = (t == (unsigned)S - 1u);
   }
   __syncthreads();
+#if GQA_DECODE_TRACE
+  tr_ticket = (unsigned long long)wall_clock64();
+  if (!s_last) trace_out(0);
+#endif
   if (!s_last) return;
   if (tid == 0) st_dev(a.counters + unit, 0u);  // ready for the next call
   if (S <= 2) {
@@ -759,6 +800,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   } else {
     merge_quads<ET, OUTF32, 1, 8>(a, prs, S, b, h0, gh, tid);
   }
+#if GQA_DECODE_TRACE
+  trace_out(1);
+#endif
 }
 
 template <int ET, int DP, bool EXACT, bool OUTF32, bool NT>

@@ -76,6 +76,11 @@ gqa_status_t check_decode_alias(const void* q, const void* k, const void* v, con
   return GQA_OK;
 }
 
+#if GQA_DECODE_TRACE
+// Timing build: where decode workgroups write their records (null: off).
+void* g_decode_trace = nullptr;
+#endif
+
 // Launch a validated decode with its plan; `workspace` holds at least
 // plan.workspace_bytes bytes (counter area first) when that is nonzero.
 gqa_status_t launch_decode_plan(const gqa::DecodePlan& plan, const void* q, const void* k,
@@ -122,6 +127,9 @@ gqa_status_t launch_decode_plan(const gqa::DecodePlan& plan, const void* q, cons
     a.counters = reinterpret_cast<unsigned*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes);
   }
+#if GQA_DECODE_TRACE
+  a.trace = static_cast<unsigned long long*>(g_decode_trace);
+#endif
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
@@ -298,6 +306,9 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pool, const void* v_p
     a.counters = reinterpret_cast<unsigned*>(workspace);
     a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes);
   }
+#if GQA_DECODE_TRACE
+  a.trace = static_cast<unsigned long long*>(g_decode_trace);
+#endif
   if (gqa::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
@@ -339,5 +350,18 @@ gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, const uint
   return gqa_prefill_band(q, k, v, mask, out, B, H, H_kv, N, M, D, 0, -1, causal ? 0 : -1,
                           in_dtype, out_dtype, stream);
 }
+
+#if GQA_DECODE_TRACE
+// Timing build only: set the buffer of kTraceRecords * 8 uint64 that the
+// decode kernels fill (null turns the trace off), and report the frequency
+// of the wall clock the records count, in kHz (0 on error).
+void gqa_debug_decode_trace(void* buffer) { g_decode_trace = buffer; }
+int gqa_debug_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+#endif
 
 }  // extern "C"

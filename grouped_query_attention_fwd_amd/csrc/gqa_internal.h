@@ -40,7 +40,12 @@ struct DecodeArgs {
   int rotate;           // 1: each workgroup starts its key walk at its own round
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
+  // timing build only (GQA_DECODE_TRACE): per-workgroup records, else null
+  unsigned long long* trace;
 };
+
+// Timing build: workgroup records of the decode trace (8 words each).
+constexpr int kTraceRecords = 8192;
 
 struct PrefillArgs {
   const void* q;
