@@ -66,6 +66,44 @@ def _library(lib, build_dir, defines):
     return outs
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libgqa_asan.so")
+# host code only: the device code of a sanitized build is the regular one
+SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+
+
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (to preload into a process that
+    loads the sanitized library)."""
+    out = _run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"]).strip().splitlines()
+    path = out[-1] if out else ""
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not hits:
+            raise RuntimeError("ASan runtime not found")
+        path = hits[-1]
+    return path
+
+
+def build_sanitized() -> str:
+    """CPU checking build: the C-ABI layer (gqa_api.hip) with its host code
+    under AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    regular kernel objects of build().  For running the ABI checks on the
+    CPU; never used on a GPU."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    if not all(os.path.exists(os.path.join(BUILD, s.replace(".hip", ".o"))) for s in SOURCES[1:]):
+        build()
+    obj = os.path.join(ASAN_DIR, "gqa_api.o")
+    _run([HIPCC, *CFLAGS, "-O1", "-g", *SANITIZE, "-Xarch_host", "-fno-omit-frame-pointer",
+          "-c", os.path.join(CSRC, "gqa_api.hip"), "-o", obj])
+    tmp = ASAN_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE, "-shared-libasan",
+          "-o", tmp, obj, *(os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES[1:])])
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def build(verbose: bool = False, trace: bool = False) -> str:
     if trace:
         outs = _library(TRACE_LIB, os.path.join(BUILD, "trace"), ["-DGQA_DECODE_TRACE=1"])

@@ -5,6 +5,8 @@
 #include "gqa_internal.h"
 
 static_assert(gqa::kCounterBytes == GQA_DECODE_COUNTER_BYTES, "counter area size");
+static_assert(sizeof(gqa_status_t) == sizeof(int) && sizeof(gqa_dtype_t) == sizeof(int),
+              "the C ABI's enums are int-sized");
 
 #include <limits.h>
 

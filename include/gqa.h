@@ -62,13 +62,23 @@
 extern "C" {
 #endif
 
+/* In C++ the enums below get int as their fixed underlying type, so that any
+ * int a C caller passes is a valid value (the library reports an unknown
+ * code as an error instead of reading an out-of-range enum).  The layout is
+ * the same as C's int-sized enums. */
+#ifdef __cplusplus
+#define GQA_ENUM_BASE : int
+#else
+#define GQA_ENUM_BASE
+#endif
+
 /* Size of the counter area at the start of a decode workspace. */
 #define GQA_DECODE_COUNTER_BYTES 16384
 
 /* Size of the fixed per-GPU scratch area of gqa_decode_noalloc (16 MiB). */
 #define GQA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
 
-typedef enum {
+typedef enum GQA_ENUM_BASE {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,        /* a required pointer is NULL                      */
   GQA_ERR_SHAPE = 2,       /* a dimension < 1, or sizes overflow the limits   */
@@ -84,7 +94,7 @@ typedef enum {
                               GQA_DECODE_NOALLOC_SCRATCH_BYTES of scratch    */
 } gqa_status_t;
 
-typedef enum {
+typedef enum GQA_ENUM_BASE {
   GQA_F32 = 0,  /* IEEE binary32                                              */
   GQA_BF16 = 1, /* bfloat16; outputs are rounded to nearest, ties to even     */
   GQA_F16 = 2   /* IEEE binary16 (half); outputs rounded to nearest even      */

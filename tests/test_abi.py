@@ -29,7 +29,9 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    return gqa.load_library()
+    # GQA_TEST_LIBRARY: run these checks against another build of the same
+    # library (the host-sanitized one, see test_sanitize_cpu.py)
+    return gqa.load_library(os.environ.get("GQA_TEST_LIBRARY") or None)
 
 
 def test_exports_match_header(lib):

@@ -59,6 +59,15 @@ SMALL = [
     # per round trip
     (45, 1, 16, 4, 65536, 128, torch.bfloat16, None),
     (46, 1, 8, 1, 40000, 64, torch.float32, "padding"),   # 1 unit, 157 splits
+    # 17 ... 32 heads per KV head: two head-chunk units per KV head
+    (47, 2, 34, 2, 1000, 128, torch.bfloat16, None),      # g = 17: chunks of 9 and 8
+    (50, 3, 64, 2, 2048, 128, torch.bfloat16, "blocks"),  # g = 32
+    # more than 32 heads per KV head: the prefill-kernel path with key splits
+    (48, 2, 48, 1, 800, 128, torch.float16, "random"),    # g = 48
+    (49, 1, 40, 1, 5000, 64, torch.float32, "padding"),   # g = 40, fp32
+    (51, 2, 128, 1, 1500, 128, torch.bfloat16, None),
+    (52, 1, 96, 1, 700, 64, torch.float32, "padding"),
+    (53, 1, 160, 2, 3000, 128, torch.float16, None),
 ]
 
 
@@ -95,7 +104,8 @@ def test_decode_empty_rows_are_nan():
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("shape", [(2, 8, 2, 4096, 128), (1, 48, 3, 999, 64), (2, 4, 4, 70, 32),
-                                   (2, 64, 2, 777, 128), (1, 64, 1, 3000, 64)])
+                                   (2, 64, 2, 777, 128), (1, 64, 1, 3000, 64),
+                                   (2, 34, 2, 500, 128), (1, 128, 1, 999, 64)])
 def test_decode_head_mapping_bit_exact(dtype, shape):
     """K = 0 and V[b, j] = j: every score is 0, every weight 1, so query head
     h must return exactly h // g (repeat-interleave, not tiling)."""

@@ -49,6 +49,9 @@ SMALL = [
     (11, 5, 32, 8, 128, 16, 5000, torch.bfloat16, "uniform"),  # several splits
     (12, 2, 4, 2, 256, 16, 700, torch.float32, "uniform"),     # fp32 D = 256
     (13, 4, 32, 8, 128, 16, 3000, torch.float16, "uniform"),   # fp16
+    (14, 5, 64, 2, 128, 16, 2500, torch.bfloat16, "uniform"),  # g = 32: two head chunks
+    (15, 3, 48, 1, 64, 32, 1500, torch.float32, [1500, 3, 700]),  # g = 48, fp32: three chunks
+    (16, 2, 128, 1, 128, 16, 900, torch.bfloat16, "uniform"),  # g = 128: eight head chunks
 ]
 
 
