@@ -551,6 +551,7 @@ def decode_trace(name, torch, reps=20):
             "event_us": e0.elapsed_time(e1) * 1e3,
             "workgroups": int(len(rec)),
             "start_spread_us": float(start.max()),
+            "plan_median_us": float(np.median(us(rec[:, 5] - rec[:, 0]))),
             "keys_done_median_us": float(np.median(keys)),
             "keys_done_max_us": float(keys.max()),
             "key_phase_median_us": float(np.median(keys - start)),

@@ -49,7 +49,8 @@ namespace {
 // 1: the timing build.  Every workgroup writes one record to a.trace:
 // wall-clock ticks at its start, when all its waves have finished their
 // keys, after its arrival ticket and at its end, where it ran (XCD, shader
-// engine, CU), its unit and split, and whether it merged.  Off in the
+// engine, CU), ticks once it knows its keys (after a paged piece plan), its
+// grid position, and whether it merged.  Off in the
 // library proper (no code at all).
 #ifndef GQA_DECODE_TRACE
 #define GQA_DECODE_TRACE 0
@@ -354,7 +355,7 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
   __shared__ __attribute__((aligned(16))) char smem_raw[C::LDS_BYTES];
 #if GQA_DECODE_TRACE
   const unsigned long long tr_start = (unsigned long long)wall_clock64();
-  unsigned long long tr_keys = 0, tr_ticket = 0;
+  unsigned long long tr_keys = 0, tr_ticket = 0, tr_plan = 0;
   const unsigned tr_wg = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   auto trace_out = [&](int merged) {
     if (threadIdx.x == 0 && a.trace != nullptr && tr_wg < (unsigned)kTraceRecords) {
@@ -366,8 +367,8 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
       r[2] = tr_ticket;
       r[3] = (unsigned long long)wall_clock64();
       r[4] = ((unsigned long long)xcc << 16) | hw;   // hw: CU in bits 11:8, SE in 14:13
-      r[5] = (unsigned long long)blockIdx.x;
-      r[6] = (unsigned long long)blockIdx.y;
+      r[5] = tr_plan;
+      r[6] = ((unsigned long long)blockIdx.x << 32) | blockIdx.y;
       r[7] = (unsigned long long)merged;
     }
   };
@@ -400,6 +401,9 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) decode_kernel(DecodeArgs
     pc.k_begin = pc.s * a.keys_per_split;
     pc.k_end = min(a.M, pc.k_begin + a.keys_per_split);
   }
+#if GQA_DECODE_TRACE
+  tr_plan = (unsigned long long)wall_clock64();
+#endif
   const int unit = __builtin_amdgcn_readfirstlane(pc.unit);
   const int s = __builtin_amdgcn_readfirstlane(pc.s);
   const int S = __builtin_amdgcn_readfirstlane(pc.S);
