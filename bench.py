@@ -116,6 +116,18 @@ def kind_of(name):
     return w.kind
 
 
+def sweep_copies(name):
+    """Input copies for a group-sweep decode: enough that the rotating set
+    exceeds the 256 MB last-level cache (at least 640 MB); 1 otherwise."""
+    import workloads
+    from grouped_query_attention_fwd_amd import accounting
+    if not name.startswith("decode_h64_"):
+        return 1
+    w = workloads.by_name(name)
+    kv = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, 2)
+    return max(1, -(-(640 << 20) // kv))
+
+
 def setup_paged(name, torch, copies=1):
     import workloads
     from grouped_query_attention_fwd_amd import accounting
@@ -572,13 +584,31 @@ def decode_trace(name, torch, reps=20):
 
 
 # ---------------------------------------------------------- counter support
+PROBE_CAL_BYTES = 256 << 20
+
+
 def profile_run(name, steps=3):
+    import ctypes
+
     import torch
     n = (1 << 30) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     y.copy_(x)                      # calibration: reads and writes exactly 1 GiB
     torch.cuda.synchronize()
+    del x, y
+    # second calibration: the read probe (read_sweep) reads exactly 256 MiB
+    lib = ctypes.CDLL(os.path.join(ROOT, "grouped_query_attention_fwd_amd", "libgqa_probe.so"))
+    lib.gqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(PROBE_CAL_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.empty(256 * 256, dtype=torch.int32, device="cuda")
+    rc = lib.gqa_probe_read(buf.data_ptr(), PROBE_CAL_BYTES, 256, 1, 8, 1, sink.data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"read probe status {rc}")
+    torch.cuda.synchronize()
+    del buf, sink
     info = setup(name, torch, copies=1)
     call = make_call(info, torch)
     for i in range(steps):
@@ -608,6 +638,13 @@ def summarize_pmc(workload, fetch_dir, write_dir):
         rows = load(d, counter)
         copy = [val for n, val in rows if "copy" in n.lower() or "elementwise" in n.lower()]
         factor = (copy_bytes / 1024.0) / max(copy) if copy and max(copy) > 0 else None
+        if counter == "FETCH_SIZE":
+            # cross-check: the read probe's 256 MiB, counted by the same counter
+            probe = [val for n, val in rows if "read_sweep" in n]
+            out["probe_read_check"] = {
+                "probe_kib_counted": max(probe) if probe else None,
+                "probe_factor": (round((PROBE_CAL_BYTES / 1024.0) / max(probe), 4)
+                                 if probe and max(probe) > 0 else None)}
         per_call = 0.0
         for pat in KERNEL_PATTERNS[kind]:
             vals = [val for n, val in rows if (pat + "<") in n or n.endswith(pat)]
@@ -692,7 +729,7 @@ def main():
     cpu_side = {"prefill_causal_n4096"} if not args.no_cpu_baseline else set()
     for name in names:
         log(f"[bench] setting up {name}")
-        info = setup(name, torch, copies=copies.get(name, 1))
+        info = setup(name, torch, copies=copies.get(name, sweep_copies(name)))
         steps = args.steps if name == primary else max(10, args.steps // 2)
         log(f"[bench] timing {name}: warmup {args.warmup}, steps {steps}")
         timing = time_workload(info, steps, args.warmup, torch)
@@ -718,7 +755,7 @@ def main():
         from grouped_query_attention_fwd_amd import accounting
         for w in workloads.GROUP_SWEEP:
             kv = accounting.decode_bytes(w.B, w.H, w.H_kv, w.M, w.D, 2)
-            copies_g = max(1, -(-(640 << 20) // kv))
+            copies_g = sweep_copies(w.name)
             log(f"[bench] group sweep {w.name} ({copies_g} copies)")
             info = setup(w.name, torch, copies=copies_g)
             timing = time_workload(info, max(10, args.steps // 2), args.warmup, torch)

@@ -399,17 +399,24 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
       // issues NKB * QB independent MFMAs, so no accumulator chain waits on
       // its own previous MFMA (measured 1 % faster than key block outermost;
       // the staged-copy kernels keep the other order, which needs fewer
-      // registers)
+      // registers).  The next step's K chunk is read before this step's
+      // MFMAs (two operand sets in turn), so its LDS latency runs under them.
+      u32x4 kop[2][C::NKB];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+        kop[0][kb] = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, qg));
 #pragma unroll
       for (int u = 0; u < C::QCH; ++u) {
-        u32x4 kop[C::NKB];
+        if (u + 1 < C::QCH) {
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+            kop[(u + 1) & 1][kb] = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * (u + 1) + qg));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
-          kop[kb] = lds_ld16(kbuf_lds, k_off<H16, DP>(16 * kb + c16, 4 * u + qg));
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) sc[qb][kb] = mma16<ET>(kop[kb], qop[qb][u], sc[qb][kb]);
+          for (int qb = 0; qb < C::QB; ++qb) sc[qb][kb] = mma16<ET>(kop[u & 1][kb], qop[qb][u], sc[qb][kb]);
       }
     } else {
 #pragma unroll
@@ -508,6 +515,21 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
     if constexpr (H16) {
 #pragma unroll
       for (int c = 0; c < C::NKB / 2; ++c) {
+        // Direct-copy kernels read this half's V operands first, so their
+        // LDS latency runs under the exps; with the K read-ahead above this
+        // took the waits for LDS reads from 16 to 5 per tile (about 2 %
+        // faster).  The staged-copy kernels hold their copy in registers and
+        // read V as they go.
+        u32x4 vops[DIRECT ? C::NDB : 1];
+        if constexpr (DIRECT) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const i16x4 ta = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c) * C::ROWB);
+            const i16x4 tb = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c + 16) * C::ROWB);
+            vops[db] = concat16(ta, tb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         u32x4 bop[C::QB];
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb) {
@@ -528,13 +550,21 @@ __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillAr
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb) lacc[qb] = mma16<ET>(ones, bop[qb], lacc[qb]);
         }
+        if constexpr (DIRECT) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const i16x4 ta = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c) * C::ROWB);
-          const i16x4 tb = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c + 16) * C::ROWB);
-          const u32x4 vop = concat16(ta, tb);
+          for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mma16<ET>(vop, bop[qb], acc[qb][db]);
+            for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mma16<ET>(vops[db], bop[qb], acc[qb][db]);
+        } else {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const i16x4 ta = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c) * C::ROWB);
+            const i16x4 tb = lds_ld_tr16(vbuf_lds, vt_off[db] + (32 * c + 16) * C::ROWB);
+            const u32x4 vop = concat16(ta, tb);
+#pragma unroll
+            for (int qb = 0; qb < C::QB; ++qb) acc[qb][db] = mma16<ET>(vop, bop[qb], acc[qb][db]);
+          }
         }
       }
       if constexpr (GQA_PREFILL_SGB && C::NKB == 4 && C::QB == 2) {
