@@ -720,7 +720,8 @@ def main():
         names += ["decode_llama70b_m32768", "prefill_causal_n4096",
                   "decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full",
                   "prefill_window4096_n16384", "prefill_chunk512_m4096",
-                  "decode_mistral7b_m4096_fp16", "prefill_causal_n4096_fp16"]
+                  "decode_mistral7b_m4096_fp16", "prefill_causal_n4096_fp16",
+                  "prefill_causal_n4096_d256"]
     copies = {"decode_mistral7b_m4096_fp16": 4, "decode_mistral7b_m4096": 4, "decode_llama70b_m32768": 1,
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}

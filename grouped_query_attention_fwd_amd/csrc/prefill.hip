@@ -89,7 +89,13 @@ struct PreCfg {
 #ifndef GQA_PREFILL_BN
 #define GQA_PREFILL_BN 64
 #endif
-  static constexpr int BN = H16 ? GQA_PREFILL_BN
+// 16-bit tiles of 256-wide rows: 32 keys, so that two workgroups fit a CU
+// (64 KB of LDS and at most 256 registers each; with 64 keys a workgroup
+// takes 128 KB of LDS and 320-380 registers, one per CU).
+#ifndef GQA_PREFILL_BN256
+#define GQA_PREFILL_BN256 32
+#endif
+  static constexpr int BN = H16 ? (DP == 256 ? GQA_PREFILL_BN256 : GQA_PREFILL_BN)
                                  : (DP <= 64 ? 64 : (DP == 128 ? 32 : 16));  // keys per tile
   static constexpr int NKB = BN / 16;
   static constexpr int NDB = DP / 16;

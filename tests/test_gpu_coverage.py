@@ -27,7 +27,7 @@ DECODES = ["decode_mistral7b_m4096", "decode_llama70b_m32768", "decode_mistral7b
            "decode_h64_g1_m4096", "decode_h64_g16_m4096", "decode_h64_g32_m4096",
            "decode_h64_g64_m4096"]
 PREFILLS = ["prefill_causal_n4096", "prefill_causal_n4096_fp16", "prefill_window4096_n16384",
-            "prefill_chunk512_m4096"]
+            "prefill_chunk512_m4096", "prefill_causal_n4096_d256"]
 PAGED = ["decode_paged_mistral7b_varlen", "decode_paged_mistral7b_full"]
 
 

@@ -134,10 +134,12 @@ def test_prefill_padded_d24_full():
     say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")
 
 
-@pytest.mark.parametrize("name", ["prefill_causal_n4096", "prefill_causal_n4096_fp16"])
+@pytest.mark.parametrize("name", ["prefill_causal_n4096", "prefill_causal_n4096_fp16",
+                                  "prefill_causal_n4096_d256"])
 def test_prefill_causal_n4096_full_sampled(name):
-    """Causal prefill (B4 H32 H_kv8 N=M=4096 D128, bf16 and fp16) at full
-    size, in the launch configuration the benchmark times.  Sampled query rows
+    """Causal prefill (B4 H32 H_kv8 N=M=4096 D128, bf16 and fp16; B2 H16
+    H_kv4 D256 bf16) at full size, in the launch configuration the benchmark
+    times.  Sampled query rows
     of every (batch row, head) are checked against the oracle, which evaluates
     a row i as an explicit mask j <= i (causal == that mask is an oracle pin)."""
     w = workloads.by_name(name)

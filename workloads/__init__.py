@@ -87,6 +87,9 @@ WORKLOADS = [
     Workload("decode_mistral7b_m4096_fp16", 10, 16, 32, 8, 1, 4096, 128, "fp16"),
     Workload("prefill_causal_n4096_fp16", 11, 4, 32, 8, 4096, 4096, 128, "fp16",
              causal=True),
+    # causal prefill with 256-wide heads (the kernel's largest head size)
+    Workload("prefill_causal_n4096_d256", 12, 2, 16, 4, 4096, 4096, 256, "bf16",
+             causal=True),
 ]
 
 
