@@ -101,6 +101,7 @@ gqa_status_t launch_decode_plan(const gqa::DecodePlan& plan, const void* q, cons
     p.mask_bs = M;
     p.splits = plan.wide_splits;
     p.kps = plan.wide_kps;
+    p.rows16 = 1;
     p.partials = plan.workspace_bytes > 0
                      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes)
                      : nullptr;

@@ -69,6 +69,7 @@ struct PrefillArgs {
   // second kernel merges them
   int splits, kps;
   float* partials;
+  int rows16;           // 1: 16 query rows per wave (the decode of large groups)
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;
 };

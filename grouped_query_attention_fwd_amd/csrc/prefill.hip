@@ -78,13 +78,15 @@ constexpr int kThreads = 64 * kWaves;
 // Rescale threshold of the online softmax, in log2 units (weights <= 2^8).
 constexpr float kLazy = 8.f;
 
-template <bool H16, int DP>
+// QBO > 0 sets the 16-row query blocks per wave (the decode of large groups
+// uses 1: its 64 heads fill all four waves of one block).
+template <bool H16, int DP, int QBO = 0>
 struct PreCfg {
   static constexpr int ELT = H16 ? 2 : 4;
 #ifndef GQA_PREFILL_QB
 #define GQA_PREFILL_QB 2
 #endif
-  static constexpr int QB = (H16 && DP <= 128) ? GQA_PREFILL_QB : 1;  // 16-row query blocks per wave
+  static constexpr int QB = QBO > 0 ? QBO : ((H16 && DP <= 128) ? GQA_PREFILL_QB : 1);  // 16-row query blocks per wave
   static constexpr int RW = 16 * QB;                       // query rows per wave
 #ifndef GQA_PREFILL_BN
 #define GQA_PREFILL_BN 64
@@ -144,11 +146,11 @@ __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
 
 // ET: element type of q, k, v.  DIRECT: 16-bit elements with D == DP, tiles
 // copied straight into LDS.  MASKED: a [B,N,M] mask is given.
-template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32>
+template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32, int QBO>
 __global__ void __launch_bounds__(kThreads, 8 / kWaves) prefill_kernel(PrefillArgs a, int HG, int units, int npb,
                                                                      int order) {
   constexpr bool H16 = ET != kF32;  // 16-bit elements: bf16 or fp16
-  using C = PreCfg<H16, DP>;
+  using C = PreCfg<H16, DP, QBO>;
   static_assert(!DIRECT || H16, "direct copies are for 16-bit tiles");
   // Two stages as two distinct LDS objects: with the loop unrolled by two
   // every access names its stage statically, so the compiler can tell that
@@ -753,9 +755,9 @@ __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArg
   }
 }
 
-template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32>
+template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32, int QBO>
 hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
-  using C = PreCfg<ET != kF32, DP>;
+  using C = PreCfg<ET != kF32, DP, QBO>;
   const int HG = (a.g % 4 == 0) ? 4 : ((a.g % 2 == 0) ? 2 : 1);
   const int PB = (kWaves / HG) * C::RW;
   const int npb = (a.N + PB - 1) / PB;
@@ -768,7 +770,7 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
     const long long last = (long long)a.N - 1 + a.q_offset + a.wr + 1;
     if (2 * max(first, 1LL) <= min(last, (long long)a.M)) order = 2;
   }
-  hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32>),
+  hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32, QBO>),
                      fold_grid(blocks, (unsigned)a.splits), dim3(kThreads), 0, stream, a, HG,
                      units, npb, order);
   hipError_t e = hipGetLastError();
@@ -780,16 +782,16 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int ET, int DP, bool OUTF32>
+template <int ET, int DP, bool OUTF32, int QBO = 0>
 hipError_t launch_dp(const PrefillArgs& a, hipStream_t stream) {
   if constexpr (ET != kF32) {
     if (a.D == DP) {
-      return a.mask ? launch_k<ET, DP, true, true, OUTF32>(a, stream)
-                    : launch_k<ET, DP, true, false, OUTF32>(a, stream);
+      return a.mask ? launch_k<ET, DP, true, true, OUTF32, QBO>(a, stream)
+                    : launch_k<ET, DP, true, false, OUTF32, QBO>(a, stream);
     }
   }
-  return a.mask ? launch_k<ET, DP, false, true, OUTF32>(a, stream)
-                : launch_k<ET, DP, false, false, OUTF32>(a, stream);
+  return a.mask ? launch_k<ET, DP, false, true, OUTF32, QBO>(a, stream)
+                : launch_k<ET, DP, false, false, OUTF32, QBO>(a, stream);
 }
 
 template <int ET, bool OUTF32>
@@ -799,6 +801,11 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   }
   if (a.D <= 32) return launch_dp<ET, 32, OUTF32>(a, stream);
   if (a.D <= 64) return launch_dp<ET, 64, OUTF32>(a, stream);
+  if constexpr (ET != kF32) {
+    // 16-row waves for the decode of large groups: a 64-head group fills one
+    // block of four waves (with 32-row waves half of them would have no row)
+    if (a.rows16 && a.D <= 128) return launch_dp<ET, 128, OUTF32, 1>(a, stream);
+  }
   if (a.D <= 128) return launch_dp<ET, 128, OUTF32>(a, stream);
   return launch_dp<ET, 256, OUTF32>(a, stream);
 }
