@@ -670,7 +670,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=3, default=None,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--hbm-read-probe", action="store_true",
-                    help="time plain torch streaming reads over 268 MB and 2 GiB")
+                    help="time the HBM read probe kernels and a torch reduction over 268 MB and 2 GiB")
     ap.add_argument("--decode-size-sweep", action="store_true",
                     help="time the Mistral-7B-shaped decode over M = 1024 ... 32768")
     ap.add_argument("--decode-trace", default=None, metavar="WORKLOAD",
