@@ -116,6 +116,7 @@ struct PreCfg {
   static constexpr int DMA_INSTS = H16 ? BN / RPI : 0;                  // per K or V tile
   static constexpr int DMA_PER_TILE = (DMA_INSTS + kWaves - 1) / kWaves;  // per wave
   static_assert(PIECES % kThreads == 0, "stage must split evenly over the threads");
+  static_assert(!H16 || BN % 32 == 0, "16-bit P.V works on whole 32-key halves of a tile");
   static_assert(!H16 || (BN % RPI == 0), "direct copy must cover whole rows");
 };
 
