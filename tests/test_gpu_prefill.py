@@ -58,6 +58,13 @@ SMALL = [
     (42, 1, 16, 2, 100, 100, 256, torch.float16, None, True),
     (43, 2, 8, 4, 129, 129, 72, torch.float16, "random", True),
     (44, 1, 3, 1, 40, 300, 32, torch.float16, "blocks", False),
+    # 256-wide 16-bit rows (eight-wave workgroups, 32-key tiles): masked,
+    # g = 3 (one head per block, 128 positions), staged rows (D = 200),
+    # a ragged key tail
+    (45, 2, 8, 2, 150, 170, 256, torch.bfloat16, "random", False),
+    (46, 1, 6, 2, 300, 300, 256, torch.bfloat16, None, True),
+    (47, 1, 8, 4, 70, 90, 200, torch.float16, "padding", True),
+    (48, 2, 4, 1, 33, 1000, 256, torch.bfloat16, "blocks", False),
 ]
 
 
