@@ -47,6 +47,9 @@ FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 (vector and matrix), published
 WARMUP_S = 0.3                   # minimum warm-up time per workload
 METRIC = "GQA decode achieved HBM GB/s (% of peak); prefill TFLOP/s (% MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# calls in the per-call timing pass (event pair around each), for its
+# median, p10 and p90
+PER_CALL_SAMPLES = 100
 KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
     "decode_paged": os.path.join(ROOT, "grouped_query_attention_fwd_amd", "csrc", "decode.hip"),
@@ -223,11 +226,13 @@ def time_workload(info, steps, warmup, torch):
     t_all1.record()
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
-    # per launch: an event pair around every call of a second timed pass
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # per launch: an event pair around every call of a second timed pass of
+    # at least PER_CALL_SAMPLES calls (median, p10 and p90 of the spread)
+    n_per = max(steps, PER_CALL_SAMPLES)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_per)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_per)]
     torch.cuda.synchronize()
-    for i in range(steps):
+    for i in range(n_per):
         starts[i].record()
         call(warmup + steps + i)
         ends[i].record()
@@ -235,6 +240,7 @@ def time_workload(info, steps, warmup, torch):
     per = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
     res = {
         "warmup_steps_done": done,
+        "per_call_samples": n_per,
         "ms_per_step": total_ms / steps,
         "launch_ms_avg": sum(per) / len(per),
         "launch_ms_p10": per[int(0.1 * (len(per) - 1))],
@@ -327,8 +333,9 @@ def result_for(info, timing):
         "workload": w.name, "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
         "ms_per_step": round(timing["ms_per_step"], 5),
         "warmup_steps_done": timing["warmup_steps_done"],
-        "launch_us": {k[len("launch_ms_"):]: round(v * 1e3, 2) for k, v in timing.items()
-                      if k.startswith("launch_ms_")},
+        "launch_us": {**{k[len("launch_ms_"):]: round(v * 1e3, 2) for k, v in timing.items()
+                         if k.startswith("launch_ms_")},
+                      "calls": timing["per_call_samples"]},
         "graph_us_per_launch": (None if timing.get("graph_ms_per_launch") is None
                                 else round(timing["graph_ms_per_launch"] * 1e3, 2)),
         "algorithmic_units_per_launch": info["units"],
