@@ -375,7 +375,8 @@ def cpu_baseline(info, budget_s=12.0, max_rows=None):
         val, unit = done_units / t_used / 1e12, "TFLOP/s"
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{rows} batch rows of {w.name} ({rows / w.B:.2f} x the workload; "
-                      f"{t_used:.1f} s of fp64 numpy on the host)"}
+                      f"{t_used:.1f} s of fp64 numpy on the host)",
+            "blas": blas_info()}
 
 
 def cpu_baseline_prefill(info, budget_s, threads, rows_per_call=256):
@@ -418,7 +419,8 @@ def cpu_baseline_prefill(info, budget_s, threads, rows_per_call=256):
             "kind": "oracle",
             "sample": f"{calls} calls of {rows_per_call} query rows x all {w.H} heads of one "
                       f"batch row of {w.name} ({flops / info['units']:.5f} x the workload's "
-                      f"flops; {t_used:.1f} s of fp64 numpy on the host)"}
+                      f"flops; {t_used:.1f} s of fp64 numpy on the host)",
+            "blas": blas_info()}
 
 
 def blas_threads():
@@ -427,6 +429,19 @@ def blas_threads():
         return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:   # noqa: BLE001
         return len(os.sched_getaffinity(0))
+
+
+def blas_info():
+    """The thread pools numpy's fp64 products ran on (threadpoolctl), and
+    the cores this process may use."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0))}
+    try:
+        from threadpoolctl import threadpool_info
+        info["pools"] = [{k: d.get(k) for k in ("user_api", "internal_api", "num_threads")}
+                         for d in threadpool_info()]
+    except Exception:   # noqa: BLE001
+        info["pools"] = None
+    return info
 
 
 # ------------------------------------------------------ calibration probes
