@@ -748,8 +748,10 @@ def main():
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}
     primary_info = None
-    # the oracle timed beside the prefill half of the metric as well
-    cpu_side = {"prefill_causal_n4096"} if not args.no_cpu_baseline else set()
+    # the oracle timed beside the prefill half of the metric and the long
+    # decode as well
+    cpu_side = ({"prefill_causal_n4096", "decode_llama70b_m32768"}
+                if not args.no_cpu_baseline else set())
     for name in names:
         log(f"[bench] setting up {name}")
         info = setup(name, torch, copies=copies.get(name, sweep_copies(name)))
