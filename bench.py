@@ -58,7 +58,8 @@ KERNEL_SOURCES = {
 }
 # the kernel one call launches (the decode merges its key splits inside the
 # kernel); a decode with more than WIDE_MIN_G heads per KV head runs as a
-# prefill over the group's heads plus a split merge (the library's plan)
+# prefill over the group's heads whose splits merge in the same launch, or
+# with a second merge kernel (the library's plan)
 WIDE_MIN_G = 32
 KERNEL_NAMES = {"decode": "decode_kernel", "decode_paged": "decode_kernel",
                 "decode_wide": "prefill_kernel", "prefill": "prefill_kernel"}

@@ -105,6 +105,7 @@ gqa_status_t launch_decode_plan(const gqa::DecodePlan& plan, const void* q, cons
     p.partials = plan.workspace_bytes > 0
                      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gqa::kCounterBytes)
                      : nullptr;
+    p.counters = plan.workspace_bytes > 0 ? reinterpret_cast<unsigned*>(workspace) : nullptr;
     p.in_type = (int)in_dtype;
     p.out_f32 = out_dtype == GQA_F32;
     if (gqa::launch_prefill(p, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;

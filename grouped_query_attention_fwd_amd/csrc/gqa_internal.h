@@ -65,10 +65,14 @@ struct PrefillArgs {
   long long mask_bs;
   // key splits: with splits > 1 workgroup column s covers keys
   // [s * kps, (s + 1) * kps) (kps a multiple of 64) and writes a partial
-  // (m, l, acc) per query row to partials [B * H * N][splits][D + 4] fp32; a
-  // second kernel merges them
+  // (m, l, acc) per query row to partials [B * H * N][splits][D + 4] fp32;
+  // the splits of a position block then merge them among themselves
+  // (counters: arrival counters and slice claims, zero between calls) or a
+  // second kernel merges them (counters null, or the launch does not allow
+  // the in-kernel merge)
   int splits, kps;
   float* partials;
+  unsigned* counters;
   int rows16;           // 1: 16 query rows per wave (the decode of large groups)
   int in_type;          // element type of q, k, v: kF32, kBF16 or kF16
   bool out_f32;

@@ -47,7 +47,12 @@
 //     causal blocks first), so the tiles in flight on an XCD stay in its L2.
 //   * Optional key splits (used by the decode of large groups, whose heads
 //     are the query rows here): workgroup column s covers one key range and
-//     writes a partial (m, l, acc) per row; a small kernel merges them.
+//     writes a partial (m, l, acc) per row.  With 16-row waves the splits of
+//     a position block merge the partials themselves, each a slice of the
+//     rows, after the last one has arrived (no second launch); otherwise a
+//     small kernel merges them.
+#include <atomic>
+
 #include "gqa_device.h"
 #include "gqa_internal.h"
 
@@ -151,6 +156,86 @@ __device__ __forceinline__ uint32_t v_off(int row, int chunk) {
   using C = PreCfg<H16, DP>;
   if constexpr (H16) return row * C::ROWB + ((chunk ^ (2 * (row & C::VSWZ))) << 4);
   else return row * C::ROWB + (chunk << 4);
+}
+
+// Bound on the polls of a workgroup that waits for the other key splits of
+// its position block (each poll is a device-scope load, at least about
+// half a microsecond): in a normal launch they all arrive within
+// microseconds; the bound only keeps the wait finite if they could not run
+// at the same time.
+constexpr int kMergeSpin = 1 << 16;
+
+// Merge rows [r0, r1) of one position block's key-split partials (`prs`:
+// rows x S splits x [m, l, -, -, acc[0..D)] fp32, read with device-scope
+// loads) into output rows orow0 + r, by `nt` threads (this one is `t`), four
+// elements of one row per item.  Splits are combined in split order, NB per
+// memory round trip (indexes clamped to the last split): a running m*, with
+// o = sum_s acc_s 2^((m_s - m*) sl) / sum_s l_s 2^((m_s - m*) sl).
+template <int ET, bool OUTF32, int NB>
+__device__ __forceinline__ void merge_rows_nb(const PrefillArgs& a, __amdgpu_buffer_rsrc_t prs,
+                                              size_t orow0, int r0, int r1, int S, int D, int t,
+                                              int nt) {
+  const float sl = kLog2e / sqrtf((float)D);
+  const int DQ = D >> 2;  // D % 4 == 0 for every supported type
+  const uint32_t sbytes = (uint32_t)(D + 4) * 4u;
+  const int n = (r1 - r0) * DQ;
+  for (int it = t; it < n; it += nt) {
+    const int rr = it / DQ;
+    const int d = 4 * (it - rr * DQ);
+    const int r = r0 + rr;
+    const uint32_t base = (uint32_t)r * (uint32_t)S * sbytes;
+    float mx = kNegInf, ls = 0.f;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      f32x2 ml[NB];
+      f32x4 pa[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const uint32_t o = base + (uint32_t)min(s0 + u, S - 1) * sbytes;
+        ml[u] = ld_dev2(prs, o);
+        pa[u] = ld_dev4(prs, o + 16u + 4u * d);
+      }
+      float cm = kNegInf;
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (s0 + u < S) cm = fmaxf(cm, ml[u][0]);
+      const float nm = fmaxf(mx, cm);
+      if (nm == kNegInf) continue;  // nothing visible yet
+      const float f0 = (mx == kNegInf) ? 0.f : exp2_hw((mx - nm) * sl);
+      ls *= f0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A[e] *= f0;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (s0 + u < S) {
+          const float f = exp2_hw((ml[u][0] - nm) * sl);
+          ls = fmaf(ml[u][1], f, ls);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) A[e] = fmaf(pa[u][e], f, A[e]);
+        }
+      }
+      mx = nm;
+    }
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = A[e] / ls;
+    const size_t oi = (orow0 + r) * (size_t)D + d;
+    if constexpr (OUTF32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = o;
+    } else {
+      u32x2 pk = {pack16<ET>(o[0], o[1]), pack16<ET>(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = pk;
+    }
+  }
+}
+
+// Up to 16 splits in one round trip, more eight at a time.
+template <int ET, bool OUTF32>
+__device__ __forceinline__ void merge_block_rows(const PrefillArgs& a, __amdgpu_buffer_rsrc_t prs,
+                                                 size_t orow0, int r0, int r1, int S, int D, int t,
+                                                 int nt) {
+  if (S <= 16) merge_rows_nb<ET, OUTF32, 16>(a, prs, orow0, r0, r1, S, D, t, nt);
+  else merge_rows_nb<ET, OUTF32, 8>(a, prs, orow0, r0, r1, S, D, t, nt);
 }
 
 // ET: element type of q, k, v.  DIRECT: 16-bit elements with D == DP, tiles
@@ -674,6 +759,16 @@ __global__ void __launch_bounds__((PreCfg<ET != kF32, DP, QBO>::THREADS),
   }
 
   // ---- epilogue: O = acc / l, or the partial of this key split -------------
+  // In-kernel merge of the key splits (16-row waves only: the decode of
+  // large groups): the partials of this position block go through
+  // device-scope stores to a region of `prows` rows x S splits.
+  const bool fused = (QBO == 1) && a.splits > 1 && a.counters != nullptr;
+  const int prows = max(0, min(PB, N - p0));
+  const uint32_t prow_bytes = (uint32_t)a.splits * (uint32_t)(D + 4) * 4u;
+  const size_t orow0 = ((size_t)b * a.H + h) * N + p0;  // the block's first output row
+  const __amdgpu_buffer_rsrc_t prs =
+      raw_rsrc(fused ? (const void*)(a.partials + orow0 * a.splits * (size_t)(D + 4)) : a.out,
+               fused ? (uint32_t)prows * prow_bytes : 0u);
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const float lt = H16 ? lacc[qb][0] : rows_sum(l_run[qb]);
@@ -682,6 +777,21 @@ __global__ void __launch_bounds__((PreCfg<ET != kF32, DP, QBO>::THREADS),
     if (a.splits > 1) {
       // record [m, l, -, -, acc[0..D)] of this row and split; m is the
       // softmax reference the weights were taken against
+      if constexpr (QBO == 1) {
+        if (fused) {
+          const uint32_t ro = (uint32_t)(pos - p0) * prow_bytes + blockIdx.y * (uint32_t)(D + 4) * 4u;
+          // words 2 and 3 of a record are zero: in row 0 they are the split's
+          // go and claim words of the merge below, cleared here before the
+          // ticket of this call
+          if (qg == 0) st_dev4(prs, ro, f32x4{m_run[qb], lt, 0.f, 0.f});
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const int d = 16 * db + 4 * qg;
+            if (d < D) st_dev4(prs, ro + 16u + 4u * d, acc[qb][db]);
+          }
+          continue;
+        }
+      }
       const size_t row = ((size_t)b * a.H + h) * N + pos;
       float* part = a.partials + (row * a.splits + blockIdx.y) * (size_t)(D + 4);
       if (qg == 0) {
@@ -711,6 +821,74 @@ __global__ void __launch_bounds__((PreCfg<ET != kF32, DP, QBO>::THREADS),
         u32x2 pk = {pack16<ET>(o[0], o[1]), pack16<ET>(o[2], o[3])};
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d) = pk;
       }
+    }
+  }
+
+  if constexpr (QBO == 1) {
+    if (!fused) return;
+    // ---- in-kernel merge of the key splits of this position block ---------
+    // The S workgroups of the block (grid column y = split) share arrival
+    // counter `arrive`; split s also owns two words of its row-0 partial
+    // record, go (word 2) and claim (word 3), zeroed with its partial.  Each
+    // workgroup stores its partial (device scope, complete before its
+    // ticket), then takes a ticket.  The last to arrive knows every partial
+    // is stored: it resets the counter, sets every other split's go word and
+    // merges its own slice of rows.  The others poll their own go word (each
+    // a different address), within a bounded spin: one that sees it sets its
+    // claim to 1 and merges its slice; one that gives up sets it to 2 and
+    // ends.  The last then waits for every claim (those splits hold tickets,
+    // so they are running, and each claim comes within its bounded spin) and
+    // merges the slices left to it.  Every output row is merged once (or,
+    // only if a claim comes later than even the last's longer bound, twice
+    // with identical values), whether or not the block's workgroups run at
+    // the same time.
+    const int S = a.splits;
+    const int sp = (int)blockIdx.y;
+    unsigned* const arrive = a.counters + L;      // merge group: (unit, position block)
+    const size_t rec = (size_t)(D + 4);           // floats per partial record
+    unsigned* const flags0 = reinterpret_cast<unsigned*>(a.partials + orow0 * S * rec) + 2;
+    const int rs = (prows + S - 1) / S;           // rows per slice
+    __shared__ int s_mode;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);         // this wave's partial stores are complete
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned t = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      int mode = 2;                               // 2: last, 1: merge own slice, 0: leave
+      if (t == (unsigned)S - 1u) {
+        st_dev(arrive, 0u);                       // ready for the next call
+      } else {
+        unsigned* const mine = flags0 + (size_t)sp * rec;
+        unsigned go = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int it = 0; go == 0u && it < kMergeSpin; ++it) {
+          __builtin_amdgcn_s_sleep(2);
+          go = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        mode = go != 0u ? 1 : 0;
+        st_dev(mine + 1, mode ? 1u : 2u);
+      }
+      s_mode = mode;
+    }
+    __syncthreads();
+    const int mode = s_mode;
+    if (mode == 0) return;
+    if (mode == 2) {
+      for (int i = tid; i < S; i += C::THREADS)
+        if (i != sp) st_dev(flags0 + (size_t)i * rec, 1u);
+    }
+    merge_block_rows<ET, OUTF32>(a, prs, orow0, sp * rs, min(prows, (sp + 1) * rs), S, D, tid,
+                                 C::THREADS);
+    if (mode != 2) return;
+    for (int i = tid; i < S; i += C::THREADS) {
+      if (i == sp) continue;
+      unsigned* const cl = flags0 + (size_t)i * rec + 1;
+      unsigned c = __hip_atomic_load(cl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int it = 0; c == 0u && it < 4 * kMergeSpin; ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        c = __hip_atomic_load(cl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (c != 1u)  // left to the last workgroup: this thread merges it alone
+        merge_block_rows<ET, OUTF32>(a, prs, orow0, i * rs, min(prows, (i + 1) * rs), S, D, 0, 1);
     }
   }
 }
@@ -765,6 +943,27 @@ __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArg
   }
 }
 
+// Workgroups of `threads` threads of `kernel` that the current device holds
+// at once (occupancy per CU x CUs), looked up once per kernel and device; 0
+// when the runtime cannot tell.
+inline long resident_workgroups(const void* kernel, int threads) {
+  constexpr int kDevs = 64;
+  static std::atomic<long> cache[kDevs];  // 0: not looked up yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kDevs) {
+    const long c = cache[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const long r = (long)per_cu * cus;
+  if (dev >= 0 && dev < kDevs && r > 0) cache[dev].store(r, std::memory_order_relaxed);
+  return r;
+}
+
 template <int ET, int DP, bool DIRECT, bool MASKED, bool OUTF32, int QBO>
 hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   using C = PreCfg<ET != kF32, DP, QBO>;
@@ -780,11 +979,26 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
     const long long last = (long long)a.N - 1 + a.q_offset + a.wr + 1;
     if (2 * max(first, 1LL) <= min(last, (long long)a.M)) order = 2;
   }
+  // The key splits merge inside the kernel (16-row waves only) when the
+  // counter area holds an arrival counter per position block and every
+  // workgroup of the launch can be resident at once (the
+  // splits of a block wait for each other; the wait is bounded, but only
+  // co-resident splits make it short).  Otherwise a second kernel merges.
+  PrefillArgs ka = a;
+  bool fused = false;
+  if constexpr (QBO == 1) {
+    fused = a.splits > 1 && a.counters != nullptr &&
+            (long)units * npb <= (long)kMaxCounters &&
+            blocks * a.splits <= resident_workgroups(
+                                     (const void*)prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32, QBO>,
+                                     C::THREADS);
+  }
+  if (!fused) ka.counters = nullptr;
   hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32, QBO>),
-                     fold_grid(blocks, (unsigned)a.splits), dim3(C::THREADS), 0, stream, a, HG,
+                     fold_grid(blocks, (unsigned)a.splits), dim3(C::THREADS), 0, stream, ka, HG,
                      units, npb, order);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess || a.splits == 1 || fused) return e;
   const long rows = (long)a.B * a.H * a.N;
   hipLaunchKernelGGL((prefill_merge_kernel<ET, OUTF32>),
                      fold_grid(rows, (unsigned)((a.D + kMergeThreads - 1) / kMergeThreads)),

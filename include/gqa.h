@@ -113,9 +113,11 @@ typedef enum GQA_ENUM_BASE {
  *   workspace: device buffer of at least gqa_decode_workspace_size(...)
  *     bytes (may be NULL when that size is 0).  Its first
  *     GQA_DECODE_COUNTER_BYTES bytes are arrival counters, one per unit of
- *     work whose keys are split over several workgroups: the last split of
- *     a unit to finish merges the unit's fp32 partial results, which follow
- *     the counters.  The counter area MUST be zero before the first call
+ *     work whose keys are split over several workgroups: once the last
+ *     split of a unit has arrived, the unit's fp32 partial results, which
+ *     follow the counters, are merged (by that split, or with more than 32
+ *     query heads per KV head by all of the unit's splits, each a slice of
+ *     its heads).  The counter area MUST be zero before the first call
  *     (zero the buffer once after allocating it); every call, of any shape
  *     and through either decode entry point, leaves it zero again, so one
  *     buffer serves every later call on the same stream that fits in it.

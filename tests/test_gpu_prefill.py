@@ -165,6 +165,26 @@ def test_prefill_causal_n4096_full_sampled(name):
         say(f"  b={b} max abs err {mx:.3e} rel rms {rr:.3e}")
 
 
+@pytest.mark.parametrize("name", ["prefill_causal_n4096", "prefill_causal_n4096_fp16"])
+def test_prefill_causal_n4096_whole_groups(name):
+    """The causal N = 4096 prefill at full size: every output row of four of
+    its 32 (batch row, KV head) groups, one per batch row and each a
+    different KV head, against the oracle run on that group alone (its g
+    query heads with their one K/V head: groups are independent in the
+    definition, so the slice is the same attention)."""
+    w = workloads.by_name(name)
+    q, k, v, mask, causal = workloads.make_inputs(w)
+    say(f"prefill causal whole groups {name}")
+    out = gqa.prefill(*to_dev(q, k, v), causal=True).cpu()
+    g = w.H // w.H_kv
+    for b, j in ((0, 0), (1, 3), (2, 5), (3, 7)):
+        hs = slice(g * j, g * (j + 1))
+        ref = oracle.gqa(np64(q[b:b + 1, hs]), np64(k[b:b + 1, j:j + 1]),
+                         np64(v[b:b + 1, j:j + 1]), None, True)
+        mx, rr = compare(out[b:b + 1, hs], ref, TOL[w.torch_dtype], f"{name} b={b} j={j}")
+        say(f"  b={b} j={j} max abs err {mx:.3e} rel rms {rr:.3e}")
+
+
 def test_prefill_grid_of_more_than_65536_workgroups():
     """1040 query heads (g = 1) of 4100 fp32 positions: 65 blocks of 64
     positions per head, 67,600 workgroups, more than one grid row holds, so
