@@ -266,23 +266,28 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
   const int U = a.B * per_b;
   const int G = a.pieces;
   const int rounds = (a.B + 63) >> 6;
-  // clamped length and 64-key groups of batch row b (0 past the last row)
+  // clamped length of batch row lane + 64 r (0 past the last row); the
+  // first 64 rows stay in a register, so the passes below do not wait on
+  // a load each (a batch of more than 64 rows re-reads the rest from cache)
   auto len_of = [&](int b) { return b < a.B ? min(max(a.kv_len[b], 0), a.M) : 0; };
+  const int len0 = len_of(lane);
+  auto len_r = [&](int r) { return r == 0 ? len0 : len_of(lane + 64 * r); };
   int N = 0, nmax = 0;
   for (int r = 0; r < rounds; ++r) {
-    const int n = (len_of(lane + 64 * r) + 63) >> 6;
+    const int n = (len_r(r) + 63) >> 6;
     N += n;
     nmax = max(nmax, n);
   }
   N = wave_sum(N) * per_b;  // the host keeps U * ceil(M / 64) below 2^30
   nmax = wave_max(nmax);
-  auto pieces_of = [&](int b, int P) {
-    const unsigned n = (unsigned)(len_of(b) + 63) >> 6;
-    return b < a.B ? (int)max(1u, (n + (unsigned)P - 1u) / (unsigned)P) : 0;
+  // pieces of round r's batch row at piece size P (0 past the last row)
+  auto pieces_of = [&](int r, int P) {
+    const unsigned n = (unsigned)(len_r(r) + 63) >> 6;
+    return lane + 64 * r < a.B ? (int)max(1u, (n + (unsigned)P - 1u) / (unsigned)P) : 0;
   };
   auto pieces_for = [&](int P) {
     int t = 0;
-    for (int r = 0; r < rounds; ++r) t += pieces_of(lane + 64 * r, P);
+    for (int r = 0; r < rounds; ++r) t += pieces_of(r, P);
     return wave_sum(t) * per_b;
   };
   int lo = max(1, (N + G - 1) / G);
@@ -315,7 +320,8 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
   int carry = 0;
   for (int r = 0; r < rounds; ++r) {
     const int b = lane + 64 * r;
-    const int sb = pieces_of(b, P);
+    const int lb = len_r(r);
+    const int sb = pieces_of(r, P);
     int incl = wave_incl_scan(sb * per_b) + carry;
     const int excl = incl - sb * per_b;
     const unsigned long long hit = __ballot(b < a.B && excl <= i && i < incl);
@@ -323,7 +329,7 @@ __device__ __forceinline__ bool paged_piece(const DecodeArgs& a, int L, Piece& p
       const int src = __builtin_ctzll(hit);
       const int S = __shfl(sb, src, 64);
       const int e0 = __shfl(excl, src, 64);
-      const int blen = len_of(64 * r + src);
+      const int blen = __shfl(lb, src, 64);
       const int nb = (blen + 63) >> 6;
       const int local = i - e0;
       const int ju = local / S;
