@@ -179,6 +179,36 @@ def test_decode_one_shot_calls_on_two_streams():
     assert torch.equal(got_small, want[0])
 
 
+@pytest.mark.parametrize("B,H,H_kv,M,dtype,mask_kind", [
+    (3, 128, 2, 2500, torch.bfloat16, None),      # 40 key splits per block of 64 heads
+    (2, 96, 2, 1000, torch.float16, None),        # 48 heads: a block of 48 rows, 16 splits
+    (2, 64, 1, 777, torch.bfloat16, "padding"),   # ragged keys, masked
+    (4, 80, 2, 4096, torch.bfloat16, None),       # 40 heads per KV head
+])
+def test_decode_large_group_in_kernel_merge(B, H, H_kv, M, dtype, mask_kind):
+    """Groups of more than 32 heads (16-bit, D = 128) run as a prefill over
+    the group's heads whose key splits merge their partials among themselves
+    in the same launch; every output against the oracle, twice in a row on
+    one workspace (the counter area is zero after each call)."""
+    say(f"large-group merge B={B} H={H} H_kv={H_kv} M={M} {dtype} mask={mask_kind}")
+    q, k, v, mask = workloads.random_case(70 + B + H, B, H, H_kv, 1, M, 128, dtype, mask_kind)
+    ref = oracle_out(q, k, v, mask)
+    qd, kd, vd, md = to_dev(q, k, v, mask)
+    n = gqa.decode_workspace_size(B, H, H_kv, M, 128)
+    assert n > gqa.DECODE_COUNTER_BYTES
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep in range(2):
+        out = gqa.decode(qd, kd, vd, md, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out, ref, TOL[dtype], f"large group rep={rep}")
+        assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0, rep
+        if first is None:
+            first = out.clone()
+        else:
+            assert torch.equal(out, first)
+
+
 def test_decode_workspace_shared_across_shapes_and_entry_points():
     """One workspace serves decode calls of different shapes, the
     large-group path and the paged form in turn: each call leaves the
@@ -188,7 +218,10 @@ def test_decode_workspace_shared_across_shapes_and_entry_points():
     say("workspace shared across shapes")
     cases = [(2, 32, 8, 4096, 128, torch.bfloat16), (1, 64, 1, 3000, 64, torch.bfloat16),
              (3, 12, 4, 777, 128, torch.float16), (2, 8, 2, 5000, 32, torch.float32),
-             (16, 32, 8, 4096, 128, torch.bfloat16)]
+             (16, 32, 8, 4096, 128, torch.bfloat16),
+             # large groups whose key splits merge in the same launch (go and
+             # claim words inside the 0xFF-filled partials): 40 and 16 splits
+             (3, 128, 2, 2500, 128, torch.bfloat16), (2, 96, 2, 1000, 128, torch.float16)]
     sizes = [gqa.decode_workspace_size(B, H, Hk, M, D) for B, H, Hk, M, D, _ in cases]
     qp, kpool, vpool, table, kl = workloads.random_paged_case(53, 4, 32, 8, 128, 16, 3000,
                                                               torch.bfloat16)
@@ -204,7 +237,7 @@ def test_decode_workspace_shared_across_shapes_and_entry_points():
                                                                  device="cuda")).clone()
     nc = gqa.DECODE_COUNTER_BYTES
     for rep in range(2):
-        for i in [4, 0, 1, 2, 3] if rep == 0 else [3, 1, 0, 4, 2]:
+        for i in [4, 0, 5, 1, 2, 6, 3] if rep == 0 else [3, 6, 1, 0, 5, 4, 2]:
             ws[nc:].fill_(0xFF)
             assert torch.equal(gqa.decode(*inputs[i], workspace=ws), fresh[i]), (rep, i)
             torch.cuda.synchronize()
