@@ -116,3 +116,29 @@ def test_band_workload_sampled_rows(name):
         for i in rows:
             ref = oracle.gqa_band(np64(q[b:b + 1, :, i:i + 1]), kb, vb, None, qo + i, wl, wr)
             compare(out[b:b + 1, :, i:i + 1], ref, TOL[torch.bfloat16], f"{name} b={b} row={i}")
+
+
+@pytest.mark.parametrize("name,b,j,r0,r1", [
+    ("prefill_chunk512_m4096", 0, 0, 0, 512),         # every row of the chunk
+    ("prefill_chunk512_m4096", 15, 7, 0, 512),
+    ("prefill_window4096_n16384", 0, 3, 8192, 9216),  # a block of 1024 rows
+    ("prefill_window4096_n16384", 0, 6, 15360, 16384),
+])
+def test_band_workload_whole_group_rows(name, b, j, r0, r1):
+    """The benchmarked banded workloads at full size: every query row in
+    [r0, r1) of the g query heads of one (batch row, KV head) group against
+    the oracle run on that group alone (groups are independent in the
+    definition; the rows' positions enter as the offset)."""
+    w = workloads.by_name(name)
+    say(f"band workload whole group {name} b={b} j={j} rows {r0}..{r1}")
+    q, k, v, mask, _ = workloads.make_inputs(w)
+    qo, wl, wr = w.band
+    qd, kd, vd = to_dev(q, k, v)
+    out = gqa.prefill_band(qd, kd, vd, None, qo, wl, wr)
+    torch.cuda.synchronize()
+    g = w.H // w.H_kv
+    hs = slice(g * j, g * (j + 1))
+    ref = oracle.gqa_band(np64(q[b:b + 1, hs, r0:r1]), np64(k[b:b + 1, j:j + 1]),
+                          np64(v[b:b + 1, j:j + 1]), None, qo + r0, wl, wr)
+    mx, rr = compare(out[b:b + 1, hs, r0:r1], ref, TOL[torch.bfloat16], f"{name} b={b} j={j}")
+    say(f"  max abs err {mx:.3e} rel rms {rr:.3e}")
