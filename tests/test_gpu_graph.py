@@ -42,10 +42,14 @@ def replay_matches(op, reps=4):
         assert torch.equal(op.out, eager), f"replay {r} differs from the eager call"
 
 
-def test_graph_decode():
-    say("graph decode")
-    q, k, v, _ = workloads.random_case(60, 4, 32, 8, 1, 4096, 128, torch.bfloat16)
-    ws = torch.zeros(gqa.decode_workspace_size(4, 32, 8, 4096, 128), dtype=torch.uint8,
+@pytest.mark.parametrize("B,H,H_kv,M", [
+    (4, 32, 8, 4096),   # key splits merged by the last split
+    (2, 64, 1, 3000),   # 64 heads per KV head: the splits merge in the prefill kernel
+])
+def test_graph_decode(B, H, H_kv, M):
+    say(f"graph decode B={B} H={H} H_kv={H_kv} M={M}")
+    q, k, v, _ = workloads.random_case(60, B, H, H_kv, 1, M, 128, torch.bfloat16)
+    ws = torch.zeros(gqa.decode_workspace_size(B, H, H_kv, M, 128), dtype=torch.uint8,
                      device="cuda")
     replay_matches(gqa.decode_op(*to_dev(q, k, v), workspace=ws))
     assert ws[:gqa.DECODE_COUNTER_BYTES].count_nonzero().item() == 0
