@@ -354,10 +354,14 @@ def cpu_baseline(info, budget_s=12.0, max_rows=None):
 
     import oracle
     threads = blas_threads()
+    if info["kind"] == "decode_paged":
+        return cpu_baseline_paged(info, budget_s, threads)
     q, k, v, mask, causal = info["cpu"]
     w = info["w"]
     if w.kind == "prefill":
-        return cpu_baseline_prefill(info, budget_s, threads)
+        # fewer rows per call where one call would take seconds (N x M above 2^26)
+        return cpu_baseline_prefill(info, budget_s, threads,
+                                    rows_per_call=64 if w.N * w.M > (1 << 26) else 256)
     done_units, t_used, rows = 0, 0.0, 0
     while t_used < budget_s and (max_rows is None or rows < max_rows):
         b = rows % w.B
@@ -376,6 +380,36 @@ def cpu_baseline(info, budget_s=12.0, max_rows=None):
         val, unit = done_units / t_used / 1e12, "TFLOP/s"
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{rows} batch rows of {w.name} ({rows / w.B:.2f} x the workload; "
+                      f"{t_used:.1f} s of fp64 numpy on the host)",
+            "blas": blas_info()}
+
+
+def cpu_baseline_paged(info, budget_s, threads):
+    """The fp64 oracle's paged decode (gather the cache through the block
+    table, then attention) on whole sequences in order, wrapping round,
+    until about budget_s seconds; throughput counts each sequence's own K/V
+    bytes, as for the GPU.  The pool is widened to float64 once, outside
+    the timed calls."""
+    import numpy as np
+
+    import oracle
+    q, kp, vp, table, lens = info["cpu"]
+    w = info["w"]
+    elt = 4 if w.dtype == "fp32" else 2
+    kp64 = kp.float().numpy().astype(np.float64)
+    vp64 = vp.float().numpy().astype(np.float64)
+    done, t_used, rows = 0, 0.0, 0
+    while t_used < budget_s:
+        b = rows % w.B
+        qb = q[b:b + 1].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.gqa_paged(qb, kp64, vp64, table[b:b + 1].numpy(), lens[b:b + 1].numpy())
+        t_used += time.perf_counter() - t0
+        done += 2 * int(lens[b]) * w.H_kv * w.D * elt
+        rows += 1
+    return {"value": round(done / t_used / 1e9, 6), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} sequences of {w.name} ({rows / w.B:.2f} x the workload; "
                       f"{t_used:.1f} s of fp64 numpy on the host)",
             "blas": blas_info()}
 
@@ -749,9 +783,10 @@ def main():
               "decode_paged_mistral7b_varlen": 4, "decode_paged_mistral7b_full": 4}
     results = {}
     primary_info = None
-    # the oracle timed beside the prefill half of the metric and the long
-    # decode as well
-    cpu_side = ({"prefill_causal_n4096", "decode_llama70b_m32768"}
+    # the oracle timed beside the prefill half of the metric, the long
+    # decode, the paged decode and the sliding window as well
+    cpu_side = ({"prefill_causal_n4096", "decode_llama70b_m32768",
+                 "decode_paged_mistral7b_varlen", "prefill_window4096_n16384"}
                 if not args.no_cpu_baseline else set())
     for name in names:
         log(f"[bench] setting up {name}")
