@@ -944,11 +944,11 @@ __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArg
 }
 
 // Workgroups of `threads` threads of `kernel` that the current device holds
-// at once (occupancy per CU x CUs), looked up once per kernel and device; 0
-// when the runtime cannot tell.
-inline long resident_workgroups(const void* kernel, int threads) {
-  constexpr int kDevs = 64;
-  static std::atomic<long> cache[kDevs];  // 0: not looked up yet
+// at once (occupancy per CU x CUs), looked up once per kernel and device
+// (`cache`: one entry per device, owned by the caller's kernel instance, 0
+// until looked up); 0 when the runtime cannot tell.
+constexpr int kDevs = 64;
+inline long resident_workgroups(const void* kernel, int threads, std::atomic<long>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < kDevs) {
@@ -987,11 +987,12 @@ hipError_t launch_k(const PrefillArgs& a, hipStream_t stream) {
   PrefillArgs ka = a;
   bool fused = false;
   if constexpr (QBO == 1) {
+    static std::atomic<long> resident[kDevs];  // this kernel instance's occupancy per device
     fused = a.splits > 1 && a.counters != nullptr &&
             (long)units * npb <= (long)kMaxCounters &&
             blocks * a.splits <= resident_workgroups(
                                      (const void*)prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32, QBO>,
-                                     C::THREADS);
+                                     C::THREADS, resident);
   }
   if (!fused) ka.counters = nullptr;
   hipLaunchKernelGGL((prefill_kernel<ET, DP, DIRECT, MASKED, OUTF32, QBO>),
